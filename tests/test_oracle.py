@@ -1,0 +1,178 @@
+"""Pins for the CPU oracle: every check here compares it with something other than itself.
+
+* exhaustive fp16 / e4m3 decode against numpy's and torch's own converters;
+* the e2m1 value table of the OCP microscaling formats;
+* hand-built superblocks whose expected weights were derived by hand from the
+  closed forms (tests/golden/blocks.json, each entry citing its passage);
+* the GEMM against numpy's fp64 matmul of the dequantized weights, and against
+  one-hot inputs (which must return a weight column exactly).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "blocks.json")
+
+
+def test_fp16_decode_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.fp16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_decode_exhaustive(orc):
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([orc.e4m3(i) for i in range(256)])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert orc.e4m3(0x01) == 2.0 ** -9     # smallest subnormal
+    assert orc.e4m3(0x7E) == 448.0         # largest finite
+
+
+def test_e2m1_table(orc):
+    # OCP MX e2m1 magnitudes for codes 0..7; bit 3 is the sign.
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(16):
+        want = -table[c & 7] if c & 8 else table[c & 7]
+        got = orc.e2m1(c)
+        assert got == want and np.signbit(got) == bool(c & 8)
+
+
+def test_nvfp4_products_exact_in_fp16(orc):
+    """The NVFP4 page states e2m1 x e4m3 fits fp16 exactly (6 of 11 significant bits)."""
+    for c in range(16):
+        for s in range(256):
+            sv = orc.e4m3(s)
+            if np.isnan(sv):
+                continue
+            v = orc.e2m1(c) * sv
+            assert float(np.float16(v)) == v
+            assert float(np.float32(v)) == v
+
+
+def test_row_bytes(orc):
+    assert orc.row_bytes(12, 2560) == 10 * 144
+    assert orc.row_bytes(13, 9728) == 38 * 176
+    assert orc.row_bytes(14, 9728) == 38 * 210
+    assert orc.row_bytes(1001, 2560) == 1280
+    assert orc.row_bytes(12, 2561) == -1
+    assert orc.row_bytes(1001, 24) == -1
+    assert orc.row_bytes(7, 256) == -1
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)["fixtures"]
+
+
+@pytest.mark.parametrize("fx", _golden(), ids=lambda f: f["name"])
+def test_golden_blocks(orc, fx):
+    data = np.frombuffer(bytes.fromhex(fx["data"]), dtype=np.uint8)
+    scales = np.frombuffer(bytes.fromhex(fx["scales"]), dtype=np.uint8) if "scales" in fx else None
+    w = orc.dequant(fx["type"], data, scales, 1, fx["k"])[0]
+    for pos, val in fx["expect"].items():
+        assert w[int(pos)] == np.float32(val), (fx["name"], pos, w[int(pos)], val)
+        assert np.signbit(w[int(pos)]) == np.signbit(val)
+
+
+def test_golden_q6k_untouched_positions(orc):
+    fx = next(f for f in _golden() if f["name"] == "q6k_A_bit_planes")
+    w = orc.dequant(14, np.frombuffer(bytes.fromhex(fx["data"]), np.uint8), None, 1, 256)[0]
+    rest = np.delete(w, [0, 32, 64, 96])
+    assert np.all(rest == -32.0)
+
+
+def test_block_and_row_stride(orc):
+    """Blocks at their 144/176/210-byte strides, and rows after rows."""
+    fx = {f["name"]: f for f in _golden()}
+    for a, b, t in (("q4k_A_nibble_order", "q4k_B_6bit_high_bits", 12),
+                    ("q5k_A_high_bit_plane", "q5k_B_scales_with_high_bits", 13),
+                    ("q6k_B_signed_scales", "q6k_C_high_two_bits", 14)):
+        A = bytes.fromhex(fx[a]["data"])
+        B = bytes.fromhex(fx[b]["data"])
+        single_a = orc.dequant(t, np.frombuffer(A, np.uint8), None, 1, 256)[0]
+        single_b = orc.dequant(t, np.frombuffer(B, np.uint8), None, 1, 256)[0]
+        mat = np.frombuffer(A + B + B + A + A + A, np.uint8)  # 2 rows x 3 blocks
+        w = orc.dequant(t, mat, None, 2, 768)
+        want = np.stack([np.concatenate([single_a, single_b, single_b]),
+                         np.concatenate([single_a, single_a, single_a])])
+        assert np.array_equal(w, want)
+        assert np.array_equal(orc.dequant(t, mat, None, 2, 768, r0=1, nr=1)[0], want[1])
+
+
+@pytest.mark.parametrize("wtype", [12, 13, 14, 1001])
+def test_gemm_matches_numpy_fp64(orc, wtype):
+    rng = synth.rng_for(123, wtype)
+    m, k, n = 24, 768, 3
+    data, scales = synth.weights(wtype, m, k, rng)
+    x = synth.activations(n, k, rng)
+    w = orc.dequant(wtype, data, scales, m, k).astype(np.float64)
+    xd = x.astype(np.float64)
+    y, a = orc.gemm(wtype, data, scales, m, k, x)
+    np.testing.assert_allclose(y, xd @ w.T, rtol=1e-12, atol=1e-12 * (np.abs(xd) @ np.abs(w).T).max())
+    np.testing.assert_allclose(a, np.abs(xd) @ np.abs(w).T, rtol=1e-12)
+    rows = np.array([5, 0, 23, 5])
+    y2, a2 = orc.gemm(wtype, data, scales, m, k, x, rows=rows)
+    assert np.array_equal(y2, y[:, rows]) and np.array_equal(a2, a[:, rows])
+
+
+@pytest.mark.parametrize("wtype", [12, 14, 1001])
+def test_gemm_one_hot_returns_column(orc, wtype):
+    rng = synth.rng_for(7, wtype)
+    m, k = 16, 512
+    data, scales = synth.weights(wtype, m, k, rng)
+    w = orc.dequant(wtype, data, scales, m, k)
+    cols = [0, 1, 255, 256, 300, 511]
+    x = np.zeros((len(cols), k), dtype=np.float16)
+    for t, c in enumerate(cols):
+        x[t, c] = 1.0
+    y, a = orc.gemm(wtype, data, scales, m, k, x)
+    for t, c in enumerate(cols):
+        assert np.array_equal(y[t], w[:, c].astype(np.float64))
+        assert np.array_equal(a[t], np.abs(w[:, c]).astype(np.float64))
+
+
+def test_gemm_thread_count_does_not_change_result(orc):
+    rng = synth.rng_for(9)
+    m, k = 64, 1024
+    data, _ = synth.weights(12, m, k, rng)
+    x = synth.activations(2, k, rng)
+    y1, _ = orc.gemm(12, data, None, m, k, x, nthreads=1)
+    assert orc.last_threads() == 1
+    y4, _ = orc.gemm(12, data, None, m, k, x, nthreads=4)
+    assert np.array_equal(y1, y4)
+
+
+def test_bad_arguments_rejected(orc):
+    data = np.zeros(144, np.uint8)
+    with pytest.raises(ValueError):
+        orc.dequant(12, data, None, 1, 100)
+    with pytest.raises(ValueError):
+        orc.dequant(1001, np.zeros(16, np.uint8), None, 1, 32)   # NVFP4 needs scales
+    with pytest.raises(ValueError):
+        orc.gemm(12, data, None, 1, 256, np.zeros((1, 128), np.float16))
+
+
+def test_generator_is_deterministic_and_in_range():
+    a, _ = synth.weights(12, 8, 512, synth.rng_for(0))
+    b, _ = synth.weights(12, 8, 512, synth.rng_for(0))
+    assert np.array_equal(a, b)
+    blocks = a.reshape(8, 2, 144)
+    d = blocks[..., 0:2].copy().view(np.float16).astype(np.float64)
+    assert d.min() >= 1e-3 * (1 - 2 ** -10) and d.max() <= 2e-2 * (1 + 2 ** -10)
+    c, s = synth.weights(1001, 4, 64, synth.rng_for(0))
+    import torch
+    sv = torch.from_numpy(s).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert sv.min() >= 0.0097 and sv.max() <= 1.0
