@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark: a Qwen3-4B-shaped decode layer of quantized projections on one MI355X.
+
+One step = one pass of the layer's projection calls over one batch of tokens:
+  qgemv_triple  Q 4096x2560 Q4_K, K 1024x2560 Q4_K, V 1024x2560 Q6_K
+  qgemv_add     Wo 2560x4096 Q4_K with the residual add
+  qgemv_pair    gate, up 9728x2560 Q4_K
+  qgemv_q6k / qgemm_rows   down 2560x9728 Q6_K
+Weights are synthetic (seeded, the value distributions of the Q4_K_M workload),
+resident in HBM before timing; 36 distinct copies of the layer (2.3 GB, beyond
+the 256 MB Infinity Cache) rotate so every step streams its weights cold.  The
+36-layer sequence is captured once in a HIP graph and replayed, so host launch
+overhead is not part of the measurement.
+
+Headline: achieved HBM GB/s (algorithmic bytes / time) at N=1, the figure the
+decode-GEMV pages care about; the same layer at N=32 is reported beside it.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+LAYERS = 36
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_q4_q5_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def call_bytes(wtype, m, k, n, resid=False):
+    import synth
+    wb = m * synth.row_bytes(wtype, k) + (m * (k // 16) if wtype == synth.NVFP4 else 0)
+    return wb + 2 * n * k + 4 * n * m + (4 * n * m if resid else 0)
+
+
+class Layer:
+    """Device buffers of one decode layer (weights shared by reference when cloned)."""
+
+    def __init__(self, W):
+        self.W = W  # name -> QWeight
+
+
+def build_layers(n_layers, seed=1):
+    import torch
+    import gemm_q4_q5_amd as qg
+    import synth
+    base = {}
+    for i, (name, wt, m, k) in enumerate(synth.QWEN3_4B_LAYER):
+        data, scales = synth.weights(wt, m, k, synth.rng_for(seed, i))
+        base[name] = qg.QWeight.from_host(wt, data, m, k, scales, device="cuda")
+    layers = [Layer(base)]
+    for _ in range(1, n_layers):
+        layers.append(Layer({nm: qg.QWeight(w.type, w.data.clone(), w.m, w.k,
+                                            None if w.scales is None else w.scales.clone())
+                             for nm, w in base.items()}))
+    torch.cuda.synchronize()
+    return layers
+
+
+class Buffers:
+    def __init__(self, n, seed=1):
+        import torch
+        import synth
+        rng = synth.rng_for(seed, 99)
+        dev = "cuda"
+        self.x_h = torch.from_numpy(synth.activations(n, 2560, rng)).to(dev)
+        self.x_o = torch.from_numpy(synth.activations(n, 4096, rng)).to(dev)
+        self.x_f = torch.from_numpy(synth.activations(n, 9728, rng)).to(dev)
+        self.resid = torch.from_numpy(rng.standard_normal((n, 2560)).astype(np.float32)).to(dev)
+        f = lambda m: torch.empty((n, m), dtype=torch.float32, device=dev)
+        self.q, self.k, self.v = f(4096), f(1024), f(1024)
+        self.o, self.g, self.u, self.d = f(2560), f(9728), f(9728), f(2560)
+
+
+def layer_calls(L, B, n):
+    """The layer's four projection calls, in order, as (name, thunk)."""
+    import gemm_q4_q5_amd as qg
+    W = L.W
+    calls = [
+        ("triple", lambda: qg.qgemv_triple(W["wq"], W["wk"], W["wv"], B.x_h, B.q, B.k, B.v)),
+        ("add", lambda: qg.qgemv_add(W["wo"], B.x_o, B.resid, B.o)),
+        ("pair", lambda: qg.qgemv_pair(W["gate"], W["up"], B.x_h, B.g, B.u)),
+    ]
+    if n == 1:
+        calls.append(("down", lambda: qg.qgemv_q6k(W["down"], B.x_f[0], B.d[0])))
+    else:
+        calls.append(("down", lambda: qg.qgemm_rows(W["down"], B.x_f, B.d)))
+    return calls
+
+
+KERNELS = ("triple", "add", "pair", "down")
+
+
+def layer_call_bytes(n):
+    return {
+        "triple": call_bytes(12, 4096, 2560, n) + call_bytes(12, 1024, 2560, n)
+        + call_bytes(14, 1024, 2560, n) - 2 * 2 * n * 2560,  # x read once for the three
+        "add": call_bytes(12, 2560, 4096, n, resid=True),
+        "pair": call_bytes(12, 9728, 2560, n) * 2 - 2 * n * 2560,
+        "down": call_bytes(14, 2560, 9728, n),
+    }
+
+
+def _capture(layers, B, n, only=None):
+    """A graph of the 36-layer rotation (all four calls, or only call `only`)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(LAYERS):
+            for name, fn in layer_calls(layers[i % len(layers)], B, n):
+                if only is None or name == only:
+                    fn()
+    return g
+
+
+def _time_graph(g, reps, wreps):
+    import torch
+    for _ in range(wreps):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def time_layer(layers, n, steps, warmup):
+    """Time the 36-layer rotation replayed from a HIP graph, then each kernel alone.
+
+    The step time comes from the graph of all four calls per layer.  Each
+    kernel's launch duration comes from a graph of that call alone over the 36
+    layers, timed with HIP events on the stream the graph runs on (HIP does not
+    allow event nodes inside a captured graph, so per-kernel events cannot sit
+    inside the step graph itself)."""
+    import torch
+    B = Buffers(n)
+    reps = max(1, (steps + LAYERS - 1) // LAYERS)
+    wreps = max(1, (warmup + LAYERS - 1) // LAYERS)
+    s = torch.cuda.Stream()   # eager warm-up on a side stream: loads code objects
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _, fn in layer_calls(layers[0], B, n):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    g = _capture(layers, B, n)
+    total_ms = _time_graph(g, reps, wreps)
+    nsteps = reps * LAYERS
+    out = {"steps": nsteps, "ms_per_step": total_ms / nsteps, "graph_replays": reps}
+    kus = {}
+    for name in KERNELS:
+        gk = _capture(layers, B, n, only=name)
+        kreps = max(1, reps // 2)
+        kus[name] = 1000.0 * _time_graph(gk, kreps, 1) / (kreps * LAYERS)
+        del gk
+    out["kernel_us"] = kus
+    return out
+
+
+def cpu_baseline(target_s=10.0):
+    """The CPU oracle on the same layer at N=1, repeated to ~target_s of work."""
+    import oracle
+    import synth
+    mats = []
+    for i, (name, wt, m, k) in enumerate(synth.QWEN3_4B_LAYER):
+        data, scales = synth.weights(wt, m, k, synth.rng_for(1, i))
+        mats.append((wt, data, scales, m, k))
+    xs = {k: synth.activations(1, k, synth.rng_for(1, 99, k)) for k in (2560, 4096, 9728)}
+    layer_bytes = sum(layer_call_bytes(1).values())
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while t < target_s:
+        for wt, data, scales, m, k in mats:
+            oracle.gemm(wt, data, scales, m, k, xs[k])
+        reps += 1
+        t = time.perf_counter() - t0
+    return {"value": layer_bytes * reps / t / 1e9, "unit": "GB/s", "cores": oracle.last_threads(),
+            "kind": "oracle",
+            "sample": f"the full decode layer (7 projections, N=1) {reps} times, {t:.1f} s; "
+                      f"oracle = plain C dequant + fp64 dot, OpenMP over rows"}
+
+
+def load_traffic(sha):
+    p = os.path.join(ROOT, "profiles", "traffic_pair.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=720)
+    ap.add_argument("--warmup", type=int, default=72)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-n32", action="store_true", help="skip the N=32 pass")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel", choices=KERNELS, default=None,
+                    help="profile mode: replay only this call over the 36-layer rotation")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per call in --kernel mode")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the product is a single-GPU kernel library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_q4_q5_amd as qg
+    qg.lib()   # fails loudly if the HIP library is not built
+    torch.cuda.set_device(0)
+
+    layers = build_layers(LAYERS)
+    if args.kernel:
+        n = args.tokens
+        B = Buffers(n)
+        for _, fn in layer_calls(layers[0], B, n):
+            fn()
+        gk = _capture(layers, B, n, only=args.kernel)
+        reps = max(1, args.steps // LAYERS)
+        ms = _time_graph(gk, reps, max(1, args.warmup // LAYERS))
+        us = 1000.0 * ms / (reps * LAYERS)
+        b = layer_call_bytes(n)[args.kernel]
+        print(json.dumps({"kernel": args.kernel, "tokens": n, "launches": reps * LAYERS,
+                          "us_per_launch": round(us, 3), "GB/s": round(b / (us * 1e3), 1),
+                          "algorithmic_bytes": b}))
+        return
+    r1 = time_layer(layers, 1, args.steps, args.warmup)
+    bytes1 = layer_call_bytes(1)
+    step_bytes = sum(bytes1.values())
+    ms = r1["ms_per_step"]
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "achieved HBM GB/s (% of peak) for Q4_K GEMV, Qwen3-4B shapes, N=1 and N=32",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": r1["steps"],
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 x 4/6-bit weights, f32 accumulate",
+        "data": "synthetic (seeded; Q4_K_M value distributions)",
+        "config": {"workload": "Qwen3-4B-shaped decode layer: QKV triple (Q4_K,Q4_K,Q6_K) + "
+                               "Wo Q4_K with residual + gate/up Q4_K pair + down Q6_K; K=2560 "
+                               "hidden, 36 distinct layers rotated (cold)", "tokens": 1,
+                   "bytes_per_step": step_bytes},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "tok_s_equiv_projections": round(1000.0 / (LAYERS * ms), 1),
+    }
+    if "kernel_us" in r1:
+        ku = r1["kernel_us"]
+        res["kernels_n1"] = {k: {"us": round(ku[k], 3), "GB/s": round(bytes1[k] / (ku[k] * 1e3), 1)}
+                             for k in ku}
+        sha = kernel_source_sha()
+        pair_us = ku["pair"]
+        ach = bytes1["pair"] / (pair_us * 1e3)
+        res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                           "traffic": load_traffic(sha), "kernel": "gemv_kernel<1> (qgemv_pair)",
+                           "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
+    if not args.no_n32:
+        r32 = time_layer(layers, 32, max(LAYERS, args.steps // 4), LAYERS)
+        b32 = layer_call_bytes(32)
+        v32 = sum(b32.values()) / (r32["ms_per_step"] * 1e-3) / 1e9
+        res["n32"] = {"value": round(v32, 2), "unit": "GB/s", "pct_of_peak": round(100 * v32 / PEAK_HBM_GBS, 2),
+                      "ms_per_step": round(r32["ms_per_step"], 5)}
+        if "kernel_us" in r32:
+            res["n32"]["kernels"] = {k: {"us": round(v, 3), "GB/s": round(b32[k] / (v * 1e3), 1)}
+                                     for k, v in r32["kernel_us"].items()}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

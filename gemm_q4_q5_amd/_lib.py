@@ -1,0 +1,198 @@
+"""ctypes binding of libqgemm.so with the C ABI's names (include/qgemm.h).
+
+Argument marshalling only: tensors supply device pointers, torch's current HIP
+stream supplies the stream, and every step of the product runs in the library's
+kernels.  Output tensors are allocated with torch when the caller passes none.
+The library must be built (gemm_q4_q5_amd.build); there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemm.so")
+
+Q4_K, Q5_K, Q6_K, NVFP4 = 12, 13, 14, 1001
+MAX_ROWS = 32
+STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_SHAPE", -3: "QG_ERR_ROWS",
+          -4: "QG_ERR_TYPE", -5: "QG_ERR_ALIGN", -6: "QG_ERR_LAUNCH"}
+
+
+class QGError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class CWeight(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("m", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgemm.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m gemm_q4_q5_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        W = ctypes.POINTER(CWeight)
+        sig = {
+            "qg_row_bytes": ([i32, i64], i64),
+            "qg_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "qg_last_error": ([], ctypes.c_char_p),
+            "qgemv_q4k": ([p, p, fp, i64, i64, p], ctypes.c_int),
+            "qgemv_q5k": ([p, p, fp, i64, i64, p], ctypes.c_int),
+            "qgemv_q6k": ([p, p, fp, i64, i64, p], ctypes.c_int),
+            "qgemv_nvfp4": ([p, p, p, fp, i64, i64, p], ctypes.c_int),
+            "qgemm_rows": ([W, p, fp, i32, p], ctypes.c_int),
+            "qgemv_add": ([W, p, fp, fp, i32, p], ctypes.c_int),
+            "qgemv_pair": ([W, W, p, fp, fp, i32, p], ctypes.c_int),
+            "qgemv_triple": ([W, W, W, p, fp, fp, fp, i32, p], ctypes.c_int),
+            "qgemv_pair_swiglu": ([W, W, p, fp, i32, p], ctypes.c_int),
+            "qdequant": ([W, fp, p], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise QGError(rc, lib().qg_last_error().decode())
+
+
+def row_bytes(wtype: int, k: int) -> int:
+    return lib().qg_row_bytes(wtype, k)
+
+
+@dataclass
+class QWeight:
+    """A quantized weight resident in device memory (raw bytes as stored)."""
+    type: int
+    data: "object"                 # torch.uint8 tensor [m, row_bytes]
+    m: int
+    k: int
+    scales: Optional[object] = None  # NVFP4 e4m3 bytes [m, k/16]
+
+    def c(self) -> CWeight:
+        return CWeight(self.type, 0, self.data.data_ptr(),
+                       self.scales.data_ptr() if self.scales is not None else None, self.m, self.k)
+
+    @classmethod
+    def from_host(cls, wtype: int, data, m: int, k: int, scales=None, device="cuda"):
+        import torch
+        d = torch.from_numpy(data).to(device)
+        s = torch.from_numpy(scales).to(device) if scales is not None else None
+        return cls(wtype, d, m, k, s)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _out(shape, like, out):
+    import torch
+    if out is not None:
+        return out
+    return torch.empty(shape, dtype=torch.float32, device=like.device)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows(x) -> int:
+    return 1 if x.dim() == 1 else x.shape[0]
+
+
+def qgemv_q4k(w: QWeight, x, y=None):
+    y = _out((w.m,), x, y)
+    _check(lib().qgemv_q4k(_ptr(w.data), _ptr(x), _ptr(y), w.m, w.k, _stream()))
+    return y
+
+
+def qgemv_q5k(w: QWeight, x, y=None):
+    y = _out((w.m,), x, y)
+    _check(lib().qgemv_q5k(_ptr(w.data), _ptr(x), _ptr(y), w.m, w.k, _stream()))
+    return y
+
+
+def qgemv_q6k(w: QWeight, x, y=None):
+    y = _out((w.m,), x, y)
+    _check(lib().qgemv_q6k(_ptr(w.data), _ptr(x), _ptr(y), w.m, w.k, _stream()))
+    return y
+
+
+def qgemv_nvfp4(w: QWeight, x, y=None):
+    y = _out((w.m,), x, y)
+    _check(lib().qgemv_nvfp4(_ptr(w.data), _ptr(w.scales), _ptr(x), _ptr(y), w.m, w.k, _stream()))
+    return y
+
+
+def qgemv(w: QWeight, x, y=None):
+    """The single-token GEMV entry point of w's type."""
+    f = {Q4_K: qgemv_q4k, Q5_K: qgemv_q5k, Q6_K: qgemv_q6k, NVFP4: qgemv_nvfp4}[w.type]
+    return f(w, x, y)
+
+
+def qgemm_rows(w: QWeight, x, y=None):
+    n = _rows(x)
+    y = _out((n, w.m), x, y)
+    cw = w.c()
+    _check(lib().qgemm_rows(ctypes.byref(cw), _ptr(x), _ptr(y), n, _stream()))
+    return y
+
+
+def qgemv_add(w: QWeight, x, resid, y=None):
+    n = _rows(x)
+    y = _out((n, w.m), x, y)
+    cw = w.c()
+    _check(lib().qgemv_add(ctypes.byref(cw), _ptr(x), _ptr(resid), _ptr(y), n, _stream()))
+    return y
+
+
+def qgemv_pair(w0: QWeight, w1: QWeight, x, y0=None, y1=None):
+    n = _rows(x)
+    y0 = _out((n, w0.m), x, y0)
+    y1 = _out((n, w1.m), x, y1)
+    c0, c1 = w0.c(), w1.c()
+    _check(lib().qgemv_pair(ctypes.byref(c0), ctypes.byref(c1), _ptr(x), _ptr(y0), _ptr(y1), n, _stream()))
+    return y0, y1
+
+
+def qgemv_triple(w0: QWeight, w1: QWeight, w2: QWeight, x, y0=None, y1=None, y2=None):
+    n = _rows(x)
+    y0 = _out((n, w0.m), x, y0)
+    y1 = _out((n, w1.m), x, y1)
+    y2 = _out((n, w2.m), x, y2)
+    c0, c1, c2 = w0.c(), w1.c(), w2.c()
+    _check(lib().qgemv_triple(ctypes.byref(c0), ctypes.byref(c1), ctypes.byref(c2), _ptr(x),
+                              _ptr(y0), _ptr(y1), _ptr(y2), n, _stream()))
+    return y0, y1, y2
+
+
+def qgemv_pair_swiglu(wg: QWeight, wu: QWeight, x, h=None):
+    n = _rows(x)
+    h = _out((n, wg.m), x, h)
+    cg, cu = wg.c(), wu.c()
+    _check(lib().qgemv_pair_swiglu(ctypes.byref(cg), ctypes.byref(cu), _ptr(x), _ptr(h), n, _stream()))
+    return h
+
+
+def qdequant(w: QWeight, out=None):
+    out = _out((w.m, w.k), w.data, out)
+    cw = w.c()
+    _check(lib().qdequant(ctypes.byref(cw), _ptr(out), _stream()))
+    return out

@@ -1,0 +1,313 @@
+// Host side of libqgemm: the C ABI declared in include/qgemm.h.
+//
+// Every entry point validates all of its arguments on the host before touching
+// the HIP runtime, so a bad call returns a QG_ERR_* code, launches nothing, and
+// can be exercised without a GPU.  The launch shape of a weight matrix is a pure
+// function of (type, m, k) (TandemLLM Kernels page, "Row invariance": tile tables
+// keyed by the weight's shape, never by the row count).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "qgemm.h"
+#include "qg_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool known_type(int32_t t) { return t == QG_Q4_K || t == QG_Q5_K || t == QG_Q6_K || t == QG_NVFP4; }
+
+const char *type_name(int32_t t) {
+    switch (t) {
+    case QG_Q4_K: return "Q4_K";
+    case QG_Q5_K: return "Q5_K";
+    case QG_Q6_K: return "Q6_K";
+    case QG_NVFP4: return "NVFP4";
+    default: return "?";
+    }
+}
+
+// Largest m * k accepted (keeps every row and element index inside the kernels'
+// 32-bit row counters and 64-bit offsets).
+constexpr int64_t kMaxM = (int64_t)1 << 30;
+constexpr int64_t kMaxK = (int64_t)1 << 20;
+
+int check_weight(const qg_weight *w, const char *name) {
+    if (!w) return fail(QG_ERR_NULL, "%s: weight descriptor is NULL", name);
+    if (!known_type(w->type)) return fail(QG_ERR_TYPE, "%s: unknown type %d", name, w->type);
+    if (w->reserved != 0) return fail(QG_ERR_TYPE, "%s: reserved field must be 0", name);
+    if (!w->data) return fail(QG_ERR_NULL, "%s: data is NULL", name);
+    if (w->type == QG_NVFP4 && !w->scales) return fail(QG_ERR_NULL, "%s: NVFP4 scales are NULL", name);
+    if (w->m < 1 || w->m > kMaxM) return fail(QG_ERR_SHAPE, "%s: m = %lld out of range", name, (long long)w->m);
+    if (w->k < 256 || w->k > kMaxK || w->k % 256)
+        return fail(QG_ERR_SHAPE, "%s: k = %lld must be a positive multiple of 256 (<= %lld)", name,
+                    (long long)w->k, (long long)kMaxK);
+    if (!aligned(w->data, 16)) return fail(QG_ERR_ALIGN, "%s: data is not 16-byte aligned", name);
+    if (w->type == QG_NVFP4 && !aligned(w->scales, 16))
+        return fail(QG_ERR_ALIGN, "%s: scales are not 16-byte aligned", name);
+    return QG_OK;
+}
+
+int check_x(const void *x) {
+    if (!x) return fail(QG_ERR_NULL, "x is NULL");
+    if (!aligned(x, 16)) return fail(QG_ERR_ALIGN, "x is not 16-byte aligned");
+    return QG_OK;
+}
+
+int check_y(const float *y, const char *name) {
+    if (!y) return fail(QG_ERR_NULL, "%s is NULL", name);
+    if (!aligned(y, 4)) return fail(QG_ERR_ALIGN, "%s is not 4-byte aligned", name);
+    return QG_OK;
+}
+
+int check_rows(int32_t n) {
+    if (n < 1 || n > QG_MAX_ROWS) return fail(QG_ERR_ROWS, "n = %d outside 1..%d", n, QG_MAX_ROWS);
+    return QG_OK;
+}
+
+// Lanes per weight row = 4 * P, a pure function of the weight's shape.  A
+// single-token call is bound by memory-level parallelism: P grows until the
+// matrix alone yields about two wavefronts per SIMD (2048 on 256 CUs) or
+// until a lane would be left with less than one superblock, and at least until
+// one lane's share of a row fits one round of loads.
+int choose_p(int32_t type, int64_t m, int64_t k) {
+    (void)type;
+    const int64_t nb = k / 256;
+    int p = 1;
+    while (p < qg::kMaxP && (nb + p - 1) / p > qg::kDepth1) p *= 2;
+    while (p < qg::kMaxP && m * p / 16 < 2048 && nb >= 2 * p) p *= 2;
+    return p;
+}
+
+int log2i(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+constexpr int kWaves = 4;            // wavefronts per workgroup
+constexpr size_t kLdsBudget = 65536;
+
+int bucket(int n) {
+    int b = 1;
+    while (b < n) b *= 2;
+    return b;
+}
+
+// Assemble and launch one gemv_kernel call over `nseg` matrices sharing x.
+int run_gemv(const qg_weight *const *w, float *const *y, const float *resid, int nseg, const void *x,
+             int32_t n, int mode, void *stream) {
+    qg::GemvArgs a;
+    memset(&a, 0, sizeof a);
+    const int64_t k = w[0]->k;
+    a.x = x;
+    a.nseg = mode == qg::MODE_SWIGLU ? 2 : nseg;
+    a.k = (int32_t)k;
+    a.nb = (int32_t)(k / 256);
+    a.n = n;
+    a.mode = mode;
+    int grid = 0, pmax = 1;
+    for (int s = 0; s < nseg; ++s) {
+        qg::Seg &g = a.seg[s];
+        g.data = (const uint8_t *)w[s]->data;
+        g.scales = (const uint8_t *)w[s]->scales;
+        g.y = y[s];
+        g.resid = s == 0 ? resid : nullptr;
+        g.row_bytes = qg_row_bytes(w[s]->type, k);
+        g.type = w[s]->type;
+        g.m = (int32_t)w[s]->m;
+        g.P = choose_p(w[s]->type, w[s]->m, k);
+        g.lp = log2i(g.P);
+        pmax = std::max(pmax, g.P);
+        const int64_t rows_per_wg = kWaves * (16 / g.P);
+        const bool counted = !(mode == qg::MODE_SWIGLU && s == 1);   // swiglu: seg 1 rides on seg 0's lanes
+        g.wg_begin = counted ? grid : a.seg[0].wg_begin;
+        if (counted) grid += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
+    }
+    if (mode == qg::MODE_SWIGLU) {
+        a.seg[1].wg_begin = 1 << 30;   // never selected by blockIdx
+        a.seg[1].y = y[0];
+    }
+    // Superblocks of x staged per LDS chunk: the whole row when it fits, else
+    // as many as the budget allows, rounded down to a multiple of P when that
+    // leaves at least P (the chunking never changes a lane's order of work).
+    const size_t per_sb = (size_t)n * (144 * 4 + 8 * 4);   // padded x pairs + sub-block sums
+    int kc = (int)std::max<size_t>(1, kLdsBudget / per_sb);
+    if (kc >= a.nb)
+        kc = a.nb;
+    else if (kc >= pmax)
+        kc = kc / pmax * pmax;
+    a.kc = kc;
+    const size_t lds = per_sb * kc;
+    int ts = 0;
+    for (int s = 0; s < nseg; ++s) ts |= qg::type_bit(w[s]->type);
+    const int nt = bucket(n);
+    // The single-token kernel stages all of x at once (up to 64 superblocks);
+    // longer rows run the multi-token kernel with n = 1 (same per-row
+    // arithmetic, chunked staging).
+    // Slots per lane: the largest share of a row any matrix of the launch gives
+    // one lane (the single-token kernel holds them all in flight at once).
+    int depth = 1;
+    for (int s = 0; s < nseg; ++s) depth = std::max(depth, (a.nb + a.seg[s].P - 1) / a.seg[s].P);
+    const bool one = nt == 1 && a.nb <= qg::kMaxNb1 && depth <= qg::kDepth1;
+    hipError_t e;
+    if (one)
+        e = depth == 1   ? qg::launch_gemv1_d1(a, ts, grid, lds, (hipStream_t)stream)
+            : depth == 2 ? qg::launch_gemv1_d2(a, ts, grid, lds, (hipStream_t)stream)
+                         : qg::launch_gemv1_d3(a, ts, grid, lds, (hipStream_t)stream);
+    else
+        e = qg::launch_gemv_ntn(a, nt == 1 ? 2 : nt, grid, lds, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+    g_err.clear();
+    return QG_OK;
+}
+
+int gemv_single(int32_t type, const void *wdata, const void *scales, const void *x, float *y, int64_t m,
+                int64_t k, void *stream) {
+    qg_weight w = {type, 0, wdata, scales, m, k};
+    int rc;
+    if ((rc = check_weight(&w, "w")) || (rc = check_x(x)) || (rc = check_y(y, "y"))) return rc;
+    const qg_weight *ws[1] = {&w};
+    float *ys[1] = {y};
+    return run_gemv(ws, ys, nullptr, 1, x, 1, qg::MODE_PLAIN, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t qg_row_bytes(int32_t type, int64_t k) {
+    if (k < 256 || k % 256) return -1;
+    switch (type) {
+    case QG_Q4_K: return k / 256 * 144;
+    case QG_Q5_K: return k / 256 * 176;
+    case QG_Q6_K: return k / 256 * 210;
+    case QG_NVFP4: return k / 2;
+    default: return -1;
+    }
+}
+
+const char *qg_status_str(int status) {
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "null pointer";
+    case QG_ERR_SHAPE: return "bad shape";
+    case QG_ERR_ROWS: return "row count out of range";
+    case QG_ERR_TYPE: return "bad tensor type";
+    case QG_ERR_ALIGN: return "misaligned pointer";
+    case QG_ERR_LAUNCH: return "launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *qg_last_error(void) { return g_err.c_str(); }
+
+int qgemv_q4k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream) {
+    return gemv_single(QG_Q4_K, w, nullptr, x, y, m, k, stream);
+}
+int qgemv_q5k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream) {
+    return gemv_single(QG_Q5_K, w, nullptr, x, y, m, k, stream);
+}
+int qgemv_q6k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream) {
+    return gemv_single(QG_Q6_K, w, nullptr, x, y, m, k, stream);
+}
+int qgemv_nvfp4(const void *codes, const void *scales, const void *x, float *y, int64_t m, int64_t k,
+                void *stream) {
+    return gemv_single(QG_NVFP4, codes, scales, x, y, m, k, stream);
+}
+
+int qgemm_rows(const qg_weight *w, const void *x, float *y, int32_t n, void *stream) {
+    int rc;
+    if ((rc = check_weight(w, "w")) || (rc = check_x(x)) || (rc = check_y(y, "y")) || (rc = check_rows(n)))
+        return rc;
+    float *ys[1] = {y};
+    return run_gemv(&w, ys, nullptr, 1, x, n, qg::MODE_PLAIN, stream);
+}
+
+int qgemv_add(const qg_weight *w, const void *x, const float *resid, float *y, int32_t n, void *stream) {
+    int rc;
+    if ((rc = check_weight(w, "w")) || (rc = check_x(x)) || (rc = check_y(y, "y")) ||
+        (rc = check_y(resid, "resid")) || (rc = check_rows(n)))
+        return rc;
+    float *ys[1] = {y};
+    return run_gemv(&w, ys, resid, 1, x, n, qg::MODE_PLAIN, stream);
+}
+
+int qgemv_pair(const qg_weight *w0, const qg_weight *w1, const void *x, float *y0, float *y1, int32_t n,
+               void *stream) {
+    int rc;
+    if ((rc = check_weight(w0, "w0")) || (rc = check_weight(w1, "w1")) || (rc = check_x(x)) ||
+        (rc = check_y(y0, "y0")) || (rc = check_y(y1, "y1")) || (rc = check_rows(n)))
+        return rc;
+    if (w0->k != w1->k) return fail(QG_ERR_SHAPE, "pair: k differs (%lld vs %lld)", (long long)w0->k, (long long)w1->k);
+    const qg_weight *ws[2] = {w0, w1};
+    float *ys[2] = {y0, y1};
+    return run_gemv(ws, ys, nullptr, 2, x, n, qg::MODE_PLAIN, stream);
+}
+
+int qgemv_triple(const qg_weight *w0, const qg_weight *w1, const qg_weight *w2, const void *x, float *y0,
+                 float *y1, float *y2, int32_t n, void *stream) {
+    int rc;
+    if ((rc = check_weight(w0, "w0")) || (rc = check_weight(w1, "w1")) || (rc = check_weight(w2, "w2")) ||
+        (rc = check_x(x)) || (rc = check_y(y0, "y0")) || (rc = check_y(y1, "y1")) || (rc = check_y(y2, "y2")) ||
+        (rc = check_rows(n)))
+        return rc;
+    if (w0->k != w1->k || w0->k != w2->k) return fail(QG_ERR_SHAPE, "triple: k differs between the weights");
+    const qg_weight *ws[3] = {w0, w1, w2};
+    float *ys[3] = {y0, y1, y2};
+    return run_gemv(ws, ys, nullptr, 3, x, n, qg::MODE_PLAIN, stream);
+}
+
+int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, float *h, int32_t n,
+                      void *stream) {
+    int rc;
+    if ((rc = check_weight(wg, "wg")) || (rc = check_weight(wu, "wu")) || (rc = check_x(x)) ||
+        (rc = check_y(h, "h")) || (rc = check_rows(n)))
+        return rc;
+    if (wg->k != wu->k || wg->m != wu->m)
+        return fail(QG_ERR_SHAPE, "swiglu pair: gate and up must have the same m and k");
+    if (wg->type != wu->type) return fail(QG_ERR_TYPE, "swiglu pair: gate and up must have the same type");
+    const qg_weight *ws[2] = {wg, wu};
+    float *ys[2] = {h, h};
+    return run_gemv(ws, ys, nullptr, 2, x, n, qg::MODE_SWIGLU, stream);
+}
+
+int qdequant(const qg_weight *w, float *out, void *stream) {
+    int rc;
+    if ((rc = check_weight(w, "w")) || (rc = check_y(out, "out"))) return rc;
+    qg::DequantArgs a;
+    memset(&a, 0, sizeof a);
+    a.data = (const uint8_t *)w->data;
+    a.scales = (const uint8_t *)w->scales;
+    a.out = out;
+    a.row_bytes = qg_row_bytes(w->type, w->k);
+    a.m = w->m;
+    a.k = (int32_t)w->k;
+    a.nb = (int32_t)(w->k / 256);
+    a.type = w->type;
+    hipError_t e = qg::launch_dequant(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+    g_err.clear();
+    return QG_OK;
+}
+
+}  // extern "C"

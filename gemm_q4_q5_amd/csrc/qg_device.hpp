@@ -1,0 +1,216 @@
+// Device-side decoders for the quantized formats, shared by every kernel of
+// libqgemm (the GEMV/rows kernel, the dequant probe and the prefill GEMM), so the
+// weights a product consumes are the weights the probe writes.
+//
+// Formats (reflex-llm kernel notes, K-quant GEMV and uint32-load sections;
+// reflex-llm Performance page, Path C and Path E; TandemLLM Kernels page, NVFP4):
+//   Q4_K 144 B: fp16 d, fp16 dmin, 12 B of packed 6-bit scale/min, 128 B quants
+//               (four 32-byte chunks; chunk c feeds sub-block 2c from its low
+//               nibbles and sub-block 2c+1 from its high nibbles).
+//   Q5_K 176 B: as Q4_K with 32 B of fifth bits ahead of the quants: bit j of
+//               byte l belongs to position l of sub-block j.
+//   Q6_K 210 B: 128 B low nibbles, 64 B high 2-bit pairs, 16 int8 scales, fp16 d.
+//   NVFP4:      e2m1 codes (low nibble = even element), e4m3 scale per 16.
+//
+// Unpacking strategy (gfx950): quants become fp16 by OR-ing them into the
+// mantissa of a power-of-two "magic" constant, so one VALU op yields two fp16
+// lanes, and v_dot2_f32_f16 then folds two weights per instruction:
+//   low nibble  q -> fp16 1024 + q       (q in mantissa bits 0..3 (+bit 4 for Q5_K))
+//   high nibble q -> fp16 256 + 4q       (q in mantissa bits 4..7 (+bit 8 for Q5_K))
+// The bias is removed once per 32-weight sub-block with the sub-block's sum of x,
+// computed by the same dot2 chain with a (1, 1) operand, so a chain over an
+// all-zero sub-block cancels to exactly 0.  Q6_K (bias 1056, not a power of two)
+// removes its bias per pair with one exact fp16 add instead.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+enum : int { T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_NVFP4 = 1001 };
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ float f16lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+
+// dot2: c + a.x*b.x + a.y*b.y (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+
+// (a & m) | o in one VALU op.  VOP3 on gfx9 takes no literal operands, so the
+// compiler splits the literal-mask form into v_and + v_or; with the constants
+// in VGPRs (hoisted out of the loops) one v_and_or_b32 does it.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(o));
+    return d;
+}
+
+// Reorder the bytes of a quant dword [b0 b1 b2 b3] to [b0 b2 b1 b3] so that the
+// 16-bit lanes of (w & 0x000F000F) hold positions (l, l+1) and those of
+// ((w >> 8) & 0x000F000F) hold (l+2, l+3).  With `sel` = kSelMis the same
+// instruction also realigns data that starts 2 bytes into `lo` (Q6_K blocks at
+// odd 210-byte offsets): logical bytes are then physical bytes 2..5 of {hi:lo}.
+constexpr uint32_t kSelAligned = 0x03010200u;
+constexpr uint32_t kSelMis = 0x05030402u;
+__device__ __forceinline__ uint32_t pair_bytes(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---------------------------------------------------------------------------
+// Q4_K / Q5_K header: the two sub-blocks j0 = 2c, j1 = 2c+1 of lane chunk c.
+// Per-lane constant selectors, set up once by kq_lane_consts().
+struct KqLane {
+    uint32_t sel;   // byte gather for the packed 6-bit table
+    uint32_t mask;  // 0x3F3F (sub-blocks 0..3) or 0x0F0F (4..7)
+    uint32_t shm;   // 0 or 4: where a min's low bits sit in its byte
+};
+
+__device__ __forceinline__ KqLane kq_lane_consts(int c) {
+    KqLane L;
+    if (c < 2) {
+        uint32_t j0 = 2 * c, j1 = 2 * c + 1;
+        L.sel = j0 | (j1 << 8) | (12u << 16) | (12u << 24);   // 12 selects 0x00
+        L.mask = 0x3F3Fu;
+        L.shm = 0;
+    } else {
+        uint32_t j0 = 2 * c - 4, j1 = 2 * c - 3;
+        L.sel = (4 + j0) | ((4 + j1) << 8) | (j0 << 16) | (j1 << 24);
+        L.mask = 0x0F0Fu;
+        L.shm = 4;
+    }
+    return L;
+}
+
+// Coefficients of the lane's two sub-blocks.  For sub-block j with sum
+// S = sum (B + s*q) x  (B the magic bias, s = 1 or 4) and X = sum x, the
+// contribution is  a*(S - B*X) + b*X  with a = d*sc/s and b = -dmin*m.
+struct KqCoef {
+    float a0, b0, a1, b1;
+};
+
+// hdr = the 16 header bytes: .x = d | dmin << 16, .y/.z/.w = scale bytes 0..11.
+// For sub-blocks 0..3, scale = low 6 bits of byte j, min = low 6 bits of byte j+4.
+// For 4..7: low 4 bits of both come from the nibbles of byte j+4 (scale low,
+// min high); their top 2 bits are bits 6..7 of bytes j-4 (scale) and j (min).
+__device__ __forceinline__ KqCoef kq_coef(uint4 hdr, const KqLane &L) {
+    uint32_t t1 = __builtin_amdgcn_perm(hdr.w, hdr.y, L.sel);   // scales
+    uint32_t t2 = __builtin_amdgcn_perm(hdr.w, hdr.z, L.sel);   // mins
+    uint32_t sc = (t1 & L.mask) | ((t1 >> 18) & 0x3030u);
+    uint32_t mn = ((t2 >> L.shm) & L.mask) | ((t2 >> 18) & 0x3030u);
+    uint32_t sm = sc | (mn << 16);
+    float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
+    KqCoef k;
+    k.a0 = d * (float)(sm & 0xFFu);
+    k.a1 = (d * 0.25f) * (float)((sm >> 8) & 0xFFu);
+    k.b0 = -dmin * (float)((sm >> 16) & 0xFFu);
+    k.b1 = -dmin * (float)(sm >> 24);
+    return k;
+}
+
+// Four fp16 pairs of one quant dword of a Q4_K/Q5_K chunk (positions l..l+3):
+// lo01/lo23 = 1024 + q (sub-block 2c), hi01/hi23 = 256 + 4q (sub-block 2c+1).
+struct Quad {
+    uint32_t lo01, lo23, hi01, hi23;
+};
+
+__device__ __forceinline__ Quad q4_quad(uint32_t w) {
+    uint32_t p = pair_bytes(w, w, kSelAligned);
+    uint32_t p8 = p >> 8;
+    Quad r;
+    r.lo01 = and_or(p, 0x000F000Fu, 0x64006400u);
+    r.lo23 = and_or(p8, 0x000F000Fu, 0x64006400u);
+    r.hi01 = and_or(p, 0x00F000F0u, 0x5C005C00u);
+    r.hi23 = and_or(p8, 0x00F000F0u, 0x5C005C00u);
+    return r;
+}
+
+// Q5_K: add the fifth bit.  hs = fifth-bit dword already shifted right by 2c and
+// byte-paired, so bit 0 of each byte belongs to sub-block 2c, bit 1 to 2c+1.
+__device__ __forceinline__ Quad q5_quad(uint32_t w, uint32_t hs) {
+    Quad r = q4_quad(w);
+    r.lo01 = and_or(hs << 4, 0x00100010u, r.lo01);
+    r.lo23 = and_or(hs >> 4, 0x00100010u, r.lo23);
+    r.hi01 = and_or(hs << 7, 0x01000100u, r.hi01);
+    r.hi23 = and_or(hs >> 1, 0x01000100u, r.hi23);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Q6_K: lane chunk c covers half s = c >> 1 and positions 16h .. 16h+15
+// (h = c & 1) of each of the four 32-weight groups g of that half.  For one
+// dword (positions l..l+3) of the low-nibble runs A (groups 0, 2) and B (groups
+// 1, 3) and of the high-bit run H, return the eight fp16 pairs q - 32, exact.
+struct Q6Oct {
+    uint32_t v[4][2];   // [group][pair]
+};
+
+__device__ __forceinline__ uint32_t q6_pair(uint32_t nib, uint32_t hb) {
+    uint32_t v = and_or(hb, 0x00300030u, and_or(nib, 0x000F000Fu, 0x64006400u));   // 1024 + q
+    h2 r = as_h2(v) + (h2){(_Float16)-1056.0f, (_Float16)-1056.0f};          // q - 32
+    return as_u32(r);
+}
+
+__device__ __forceinline__ Q6Oct q6_oct(uint32_t a, uint32_t b, uint32_t hq) {
+    // a, b, hq already byte-paired ([b0 b2 b1 b3]).
+    uint32_t a8 = a >> 8, b8 = b >> 8, h8 = hq >> 8;
+    Q6Oct o;
+    o.v[0][0] = q6_pair(a, hq << 4);
+    o.v[0][1] = q6_pair(a8, h8 << 4);
+    o.v[1][0] = q6_pair(b, hq << 2);
+    o.v[1][1] = q6_pair(b8, h8 << 2);
+    o.v[2][0] = q6_pair(a >> 4, hq);
+    o.v[2][1] = q6_pair(a8 >> 4, h8);
+    o.v[3][0] = q6_pair(b >> 4, hq >> 2);
+    o.v[3][1] = q6_pair(b8 >> 4, h8 >> 2);
+    return o;
+}
+
+// Signed 8-bit field at bit `off` of w (an int8 Q6_K scale), as fp32.
+__device__ __forceinline__ float i8_at(uint32_t w, int off) {
+    return (float)(int32_t)__builtin_amdgcn_sbfe(w, off, 8);
+}
+
+// Q6_K sub-block scales of lane half h: the int8 scales h, h+2 (in l0) and h+4,
+// h+6 (in l1 = the next four bytes), each multiplied by d (exact in fp32).
+__device__ __forceinline__ void q6_coefs(uint32_t l0, uint32_t l1, float d, int h, float (&coef)[4]) {
+    const int sh = 8 * h;
+    coef[0] = d * i8_at(l0, sh);
+    coef[1] = d * i8_at(l0, sh + 16);
+    coef[2] = d * i8_at(l1, sh);
+    coef[3] = d * i8_at(l1, sh + 16);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4: one code byte -> two fp16 values (low nibble first), exact e2m1.
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, int byte) {
+    h2 v;
+    switch (byte) {
+    case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0); break;
+    case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1); break;
+    case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2); break;
+    default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3); break;
+    }
+    return as_u32(v);
+}
+
+// OCP E4M3FN byte `byte` of w -> fp32 (exact).
+__device__ __forceinline__ float e4m3_at(uint32_t w, int byte) {
+    switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+    }
+}
+
+}  // namespace qg

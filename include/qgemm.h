@@ -1,0 +1,177 @@
+/*
+ * qgemm.h -- C ABI of libqgemm.so, the fused dequantize-in-registers product
+ *
+ *     y[n x m] = x[n x k] . W^T        (W quantized, x fp16, y fp32)
+ *
+ * for GGML K-quant weights (Q4_K, Q5_K, Q6_K) and NVFP4 W4A16 weights, on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, then section):
+ *  [KN]  reflex-llm kernel notes (docs/kernels.md): the K-quant GEMV, the
+ *        uint32 weight-load variant with its residual-add / pair / triple
+ *        kernels, and the batched multi-token GEMM.
+ *  [PF]  reflex-llm Performance page: Path C (Q4_K uint32 decode loads, the
+ *        210-byte Q6_K block), Path E / E5 (tensor-core Q4_K prefill GEMM).
+ *  [TK]  TandemLLM Kernels page: "Row invariance", "Verify twins",
+ *        "NVFP4 matrix products", "Head, norms, attention".
+ *
+ * Conventions shared by every entry point
+ *  - All buffer pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, frees nothing and keeps no mutable state; calls may be
+ *    made from several host threads at once.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work
+ *    and return; results are ready when the stream reaches that point.
+ *  - x is fp16, row-major [n][k], contiguous.  y and resid are fp32 row-major
+ *    [n][m]: output (token t, weight row r) is y[t*m + r]  ([KN] batched GEMM,
+ *    output layout).
+ *  - W is stored exactly as the format defines, rows contiguous:
+ *      Q4_K: 144-byte superblocks of 256 weights: fp16 d, fp16 dmin, 12 bytes
+ *            of packed 6-bit sub-block scales/mins, 128 bytes of 4-bit quants;
+ *      Q5_K: 176-byte superblocks: as Q4_K plus 32 bytes of fifth quant bits
+ *            (placed before the 128 quant bytes);
+ *      Q6_K: 210-byte superblocks: 128 bytes of low 4 bits, 64 bytes of high
+ *            2 bits, 16 int8 sub-block scales, fp16 d;
+ *      NVFP4: `data` = e2m1 codes [m][k/2] (element k in byte k/2, low nibble
+ *            for even k); `scales` = e4m3 (OCP E4M3FN) [m][k/16], one per 16
+ *            consecutive weights of a row.
+ *    Weight value: Q4_K/Q5_K  d*sc[j]*q - dmin*min[j]  ([PF] Path E);
+ *                  Q6_K       d*sc[j]*(q - 32);
+ *                  NVFP4      e2m1(code) * e4m3(scale)  ([TK] NVFP4).
+ *    Row r of a K-quant weight starts at data + r * qg_row_bytes(type, k).
+ *  - k must be a multiple of 256 for every type (one superblock; for NVFP4 one
+ *    block of 16 scales).  m >= 1.
+ *  - Alignment: data, scales and x 16-byte aligned; y and resid 4-byte aligned.
+ *  - Errors: every argument is checked on the host BEFORE anything is enqueued;
+ *    on error nothing is launched and a negative QG_ERR_* code is returned, with
+ *    a description in qg_last_error() (thread-local).  There is no fallback
+ *    kernel.  Weight contents are not validated (NaN codes propagate).
+ *  - Aliasing: resid may equal y (in-place residual add); any other overlap
+ *    between an output and another buffer is undefined.
+ *  - Determinism and row invariance ([TK] Row invariance, Verify twins): the
+ *    per-row instruction sequence and the reduction order depend only on
+ *    (type, m, k), never on n or on the other rows.  For 1 <= n <= 32 the
+ *    qgemv_* / qgemm_rows / fused calls therefore give bit-identical results
+ *    for a given row whether it is called alone (n = 1) or as one of n rows,
+ *    each output of a pair/triple equals the corresponding single call bit for
+ *    bit, and qgemv_add equals fl32(resid + qgemm_rows(...)).  Repeated calls
+ *    return identical bits.  qgemm_prefill is deterministic but carries no such
+ *    twin contract ([TK] "Prefill kernels": chunk kernels share work across rows).
+ *  - Accuracy: fp32 accumulation; |y - y_exact| stays far inside
+ *    2e-3 * sum_k |w||x| for the documented value ranges.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tensor type codes.  12 and 14 are the GGML type numbers of Q4_K and Q6_K that
+ * [PF] Path C's typed kernels are instantiated with (<12>, <12,12>, <12,12,14>);
+ * 13 (Q5_K) sits between them; NVFP4 has no GGML number and takes 1001. */
+typedef enum {
+    QG_Q4_K = 12,
+    QG_Q5_K = 13,
+    QG_Q6_K = 14,
+    QG_NVFP4 = 1001
+} qg_type;
+
+/* Status codes. */
+#define QG_OK            0
+#define QG_ERR_NULL     -1   /* a required pointer is NULL                        */
+#define QG_ERR_SHAPE    -2   /* m < 1, k not a multiple of 256, k mismatch, n < 1 */
+#define QG_ERR_ROWS     -3   /* n outside 1..QG_MAX_ROWS for a row-invariant call */
+#define QG_ERR_TYPE     -4   /* unknown type, or a type the call does not take    */
+#define QG_ERR_ALIGN    -5   /* a pointer violates the alignment rules            */
+#define QG_ERR_LAUNCH   -6   /* the HIP runtime refused the launch                */
+
+#define QG_MAX_ROWS 32       /* largest n of the row-invariant calls ([KN] GEMM_MAX_BATCH) */
+
+/* A quantized weight matrix (m rows of k weights).  `scales` is used by NVFP4
+ * only and must be NULL-free for it; it is ignored for the K-quants. */
+typedef struct qg_weight {
+    int32_t type;        /* a qg_type                                   */
+    int32_t reserved;    /* must be 0                                   */
+    const void *data;    /* superblocks, or NVFP4 codes                 */
+    const void *scales;  /* NVFP4 e4m3 scales [m][k/16]; else unused    */
+    int64_t m;           /* rows (output features)                      */
+    int64_t k;           /* columns (reduction length)                  */
+} qg_weight;
+
+/* Bytes of one stored weight row (NVFP4: of the codes only); -1 if the type is
+ * unknown or k is not a multiple of 256. */
+int64_t qg_row_bytes(int32_t type, int64_t k);
+
+/* Static text for a status code. */
+const char *qg_status_str(int status);
+
+/* Description of the last error raised on the calling thread ("" if none). */
+const char *qg_last_error(void);
+
+/*
+ * Single-token GEMV, one call per weight type ([KN] K-quant GEMV: y[M] = W[MxK] x[K];
+ * the dispatcher there selects the kernel by GGML tensor type).
+ *   w: m rows of the named type; x: fp16 [k]; y: fp32 [m].
+ * Bit-identical to qgemm_rows with n = 1 on the same weight ([KN]: N = 1 routes to
+ * the GEMV so the decode path is bit-identical).
+ */
+int qgemv_q4k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream);
+int qgemv_q5k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream);
+int qgemv_q6k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream);
+
+/* NVFP4 W4A16 GEMV ([TK] NVFP4 matrix products): codes [m][k/2], scales e4m3
+ * [m][k/16], x fp16 [k], y fp32 [m]. */
+int qgemv_nvfp4(const void *codes, const void *scales, const void *x, float *y,
+                int64_t m, int64_t k, void *stream);
+
+/*
+ * Row-invariant multi-token product, 1 <= n <= 32 ([KN] batched GEMM: weights are
+ * streamed once for n tokens; [TK] Verify twins: the n-row call equals n one-row
+ * calls bit for bit).  x fp16 [n][k], y fp32 [n][m].
+ */
+int qgemm_rows(const qg_weight *w, const void *x, float *y, int32_t n, void *stream);
+
+/*
+ * Residual-fused product ([KN] gemv_quant_add: the Wo projection with the residual
+ * add folded in):  y[t][r] = fl32(resid[t][r] + (x W^T)[t][r]),  1 <= n <= 32.
+ * resid may be the same buffer as y.
+ */
+int qgemv_add(const qg_weight *w, const void *x, const float *resid, float *y,
+              int32_t n, void *stream);
+
+/*
+ * Two products sharing x in one launch ([KN] gemv_quant_pair: gate and up).
+ * w0->k must equal w1->k; types may differ.  y0 [n][w0->m], y1 [n][w1->m].
+ */
+int qgemv_pair(const qg_weight *w0, const qg_weight *w1, const void *x,
+               float *y0, float *y1, int32_t n, void *stream);
+
+/*
+ * Three products sharing x in one launch ([KN] gemv_quant_triple: Q, K, V with
+ * the Q4_K/Q4_K/Q6_K mix of Qwen3-4B Q4_K_M).  All k equal; types may differ.
+ */
+int qgemv_triple(const qg_weight *w0, const qg_weight *w1, const qg_weight *w2,
+                 const void *x, float *y0, float *y1, float *y2, int32_t n, void *stream);
+
+/*
+ * Gate/up pair with the SwiGLU activation fused into its epilogue ([KN] SwiGLU:
+ * out = silu(gate) * up, silu(g) = g / (1 + exp(-g))):
+ *   h[t][r] = silu((x Wg^T)[t][r]) * (x Wu^T)[t][r],  1 <= n <= 32.
+ * wg and wu must have the same m and k.  h fp32 [n][m].  The two products are
+ * the bits of qgemv_pair; the activation adds one fp32 evaluation.
+ */
+int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
+                      float *h, int32_t n, void *stream);
+
+/*
+ * Decoder probe: out[r][k] = the fp32 weight value of row r, column k, for every
+ * element (the device decoders the products use).  out fp32 [m][k].
+ */
+int qdequant(const qg_weight *w, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMM_H */

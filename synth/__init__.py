@@ -55,8 +55,12 @@ def _put_u16(blocks: np.ndarray, off: int, bits: np.ndarray) -> None:
 
 
 def kquant_weights(wtype: int, m: int, k: int, rng: np.random.Generator,
-                   d_range=(1e-3, 2e-2)) -> np.ndarray:
-    """Random K-quant weight matrix as raw bytes, shape [m, row_bytes]."""
+                   d_range=(1e-3, 2e-2), q6_scale_range=(0, 64)) -> np.ndarray:
+    """Random K-quant weight matrix as raw bytes, shape [m, row_bytes].
+
+    q6_scale_range is the half-open integer range of the Q6_K int8 scales
+    ((-128, 128) covers every code).
+    """
     if k % QK:
         raise ValueError("k must be a multiple of 256")
     nb = k // QK
@@ -67,7 +71,9 @@ def kquant_weights(wtype: int, m: int, k: int, rng: np.random.Generator,
         _put_u16(blocks, 0, _fp16_bits(rng.uniform(lo, hi, size=(m, nb))))
         _put_u16(blocks, 2, _fp16_bits(rng.uniform(lo, hi, size=(m, nb))))
     elif wtype == Q6_K:
-        blocks[..., 192:208] = rng.integers(0, 64, size=(m, nb, 16), dtype=np.uint8)
+        lo, hi = q6_scale_range
+        blocks[..., 192:208] = rng.integers(lo, hi, size=(m, nb, 16)).astype(np.int8).view(np.uint8)
+        lo, hi = d_range
         _put_u16(blocks, 208, _fp16_bits(rng.uniform(lo, hi, size=(m, nb))))
     else:
         raise ValueError(f"not a K-quant type: {wtype}")
@@ -95,11 +101,11 @@ def activations(n: int, k: int, rng: np.random.Generator) -> np.ndarray:
     return rng.standard_normal(size=(n, k)).astype(np.float16)
 
 
-def weights(wtype: int, m: int, k: int, rng: np.random.Generator):
+def weights(wtype: int, m: int, k: int, rng: np.random.Generator, **kw):
     """(data, scales-or-None) for any supported type."""
     if wtype == NVFP4:
-        return nvfp4_weights(m, k, rng)
-    return kquant_weights(wtype, m, k, rng), None
+        return nvfp4_weights(m, k, rng, **kw)
+    return kquant_weights(wtype, m, k, rng, **kw), None
 
 
 def duplicate_rows(x: np.ndarray) -> np.ndarray:
