@@ -150,7 +150,7 @@ int run_gemv(const qg_weight *const *w, float *const *y, const float *resid, int
     // Superblocks of x staged per LDS chunk: the whole row when it fits, else
     // as many as the budget allows, rounded down to a multiple of P when that
     // leaves at least P (the chunking never changes a lane's order of work).
-    const size_t per_sb = (size_t)n * (144 * 4 + 8 * 4);   // padded x pairs + sub-block sums
+    const size_t per_sb = (size_t)n * (144 * 4 + 16 * 4);   // padded x pairs + x sums
     int kc = (int)std::max<size_t>(1, kLdsBudget / per_sb);
     if (kc >= a.nb)
         kc = a.nb;

@@ -47,10 +47,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs A) {
                                    pair_bytes(hv[i + 1], hv[i], sel));
             for (int g = 0; g < 4; ++g) {
                 const int pos = 128 * s + 32 * g + 16 * h + 4 * i;
-                out[pos] = coef[g] * f16lo(o.v[g][0]);
-                out[pos + 1] = coef[g] * f16hi(o.v[g][0]);
-                out[pos + 2] = coef[g] * f16lo(o.v[g][1]);
-                out[pos + 3] = coef[g] * f16hi(o.v[g][1]);
+                // coef[g] * (v - bias) = d * sc * (q - 32), every step exact.
+                const float bias = g < 2 ? 1056.0f : 384.0f;
+                out[pos] = coef[g] * (f16lo(o.v[g][0]) - bias);
+                out[pos + 1] = coef[g] * (f16hi(o.v[g][0]) - bias);
+                out[pos + 2] = coef[g] * (f16lo(o.v[g][1]) - bias);
+                out[pos + 3] = coef[g] * (f16hi(o.v[g][1]) - bias);
             }
         }
     } else {

@@ -19,8 +19,8 @@
 //   high nibble q -> fp16 256 + 4q       (q in mantissa bits 4..7 (+bit 8 for Q5_K))
 // The bias is removed once per 32-weight sub-block with the sub-block's sum of x,
 // computed by the same dot2 chain with a (1, 1) operand, so a chain over an
-// all-zero sub-block cancels to exactly 0.  Q6_K (bias 1056, not a power of two)
-// removes its bias per pair with one exact fp16 add instead.
+// all-zero sub-block cancels to exactly 0.  Q6_K centres q at 32; its bias
+// (1056 or 384, not powers of two) is removed the same way, per 16-weight group.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -47,11 +47,11 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // (a & m) | o in one VALU op.  VOP3 on gfx9 takes no literal operands, so the
-// compiler splits the literal-mask form into v_and + v_or; with the constants
-// in VGPRs (hoisted out of the loops) one v_and_or_b32 does it.
+// compiler splits the literal-mask form into v_and + v_or; with the mask in an
+// SGPR (one scalar operand is allowed) and o in a VGPR, one v_and_or_b32 does it.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
     uint32_t d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(o));
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(o));
     return d;
 }
 
@@ -149,29 +149,28 @@ __device__ __forceinline__ Quad q5_quad(uint32_t w, uint32_t hs) {
 // Q6_K: lane chunk c covers half s = c >> 1 and positions 16h .. 16h+15
 // (h = c & 1) of each of the four 32-weight groups g of that half.  For one
 // dword (positions l..l+3) of the low-nibble runs A (groups 0, 2) and B (groups
-// 1, 3) and of the high-bit run H, return the eight fp16 pairs q - 32, exact.
+// 1, 3) and of the high-bit run H, build the eight fp16 pairs:
+//   groups 0, 1: 1024 + q  (low nibble in bits 0..3, high bits in 4..5);
+//   groups 2, 3: 256 + 4q  (low nibble already in bits 4..7, high bits in 8..9),
+// so one shift of H serves two groups.  q - 32 is recovered per group by
+// subtracting 1056 (resp. 384) times the group's sum of x (see q6_coefs).
 struct Q6Oct {
     uint32_t v[4][2];   // [group][pair]
 };
 
-__device__ __forceinline__ uint32_t q6_pair(uint32_t nib, uint32_t hb) {
-    uint32_t v = and_or(hb, 0x00300030u, and_or(nib, 0x000F000Fu, 0x64006400u));   // 1024 + q
-    h2 r = as_h2(v) + (h2){(_Float16)-1056.0f, (_Float16)-1056.0f};          // q - 32
-    return as_u32(r);
-}
-
 __device__ __forceinline__ Q6Oct q6_oct(uint32_t a, uint32_t b, uint32_t hq) {
     // a, b, hq already byte-paired ([b0 b2 b1 b3]).
-    uint32_t a8 = a >> 8, b8 = b >> 8, h8 = hq >> 8;
+    const uint32_t a8 = a >> 8, b8 = b >> 8, h8 = hq >> 8;
+    const uint32_t h4 = hq << 4, h2 = hq << 2, h84 = h8 << 4, h82 = h8 << 2;
     Q6Oct o;
-    o.v[0][0] = q6_pair(a, hq << 4);
-    o.v[0][1] = q6_pair(a8, h8 << 4);
-    o.v[1][0] = q6_pair(b, hq << 2);
-    o.v[1][1] = q6_pair(b8, h8 << 2);
-    o.v[2][0] = q6_pair(a >> 4, hq);
-    o.v[2][1] = q6_pair(a8 >> 4, h8);
-    o.v[3][0] = q6_pair(b >> 4, hq >> 2);
-    o.v[3][1] = q6_pair(b8 >> 4, h8 >> 2);
+    o.v[0][0] = and_or(h4, 0x00300030u, and_or(a, 0x000F000Fu, 0x64006400u));
+    o.v[0][1] = and_or(h84, 0x00300030u, and_or(a8, 0x000F000Fu, 0x64006400u));
+    o.v[1][0] = and_or(h2, 0x00300030u, and_or(b, 0x000F000Fu, 0x64006400u));
+    o.v[1][1] = and_or(h82, 0x00300030u, and_or(b8, 0x000F000Fu, 0x64006400u));
+    o.v[2][0] = and_or(h4, 0x03000300u, and_or(a, 0x00F000F0u, 0x5C005C00u));
+    o.v[2][1] = and_or(h84, 0x03000300u, and_or(a8, 0x00F000F0u, 0x5C005C00u));
+    o.v[3][0] = and_or(h2, 0x03000300u, and_or(b, 0x00F000F0u, 0x5C005C00u));
+    o.v[3][1] = and_or(h82, 0x03000300u, and_or(b8, 0x00F000F0u, 0x5C005C00u));
     return o;
 }
 
@@ -180,14 +179,17 @@ __device__ __forceinline__ float i8_at(uint32_t w, int off) {
     return (float)(int32_t)__builtin_amdgcn_sbfe(w, off, 8);
 }
 
-// Q6_K sub-block scales of lane half h: the int8 scales h, h+2 (in l0) and h+4,
-// h+6 (in l1 = the next four bytes), each multiplied by d (exact in fp32).
+// Q6_K group coefficients of lane half h: the int8 scales h, h+2 (in l0) and
+// h+4, h+6 (in l1 = the next four bytes).  For group g with dot2 sum S over its
+// magic pairs and X the same chain over x alone, the group adds
+//   a_g * (S - B_g * X),  B_g = 1056 (g < 2) or 384 (g >= 2),
+//   a_g = d * sc_g (g < 2) or d * sc_g / 4 (g >= 2).
 __device__ __forceinline__ void q6_coefs(uint32_t l0, uint32_t l1, float d, int h, float (&coef)[4]) {
     const int sh = 8 * h;
     coef[0] = d * i8_at(l0, sh);
     coef[1] = d * i8_at(l0, sh + 16);
-    coef[2] = d * i8_at(l1, sh);
-    coef[3] = d * i8_at(l1, sh + 16);
+    coef[2] = (d * 0.25f) * i8_at(l1, sh);
+    coef[3] = (d * 0.25f) * i8_at(l1, sh + 16);
 }
 
 // ---------------------------------------------------------------------------

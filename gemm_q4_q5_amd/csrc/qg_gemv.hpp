@@ -118,7 +118,8 @@ __device__ __forceinline__ RawF4 load_f4(const uint8_t *codes, const uint8_t *sc
 //   Q4_K / Q5_K / NVFP4 lanes read at pair offsets 32c (+144 per superblock):
 //     pad after every 32 pairs;
 //   Q6_K lanes read at 64s + 8h: pad after every 64 pairs.
-constexpr int kSbDw = 144;   // LDS dwords per staged superblock and token
+constexpr int kSbDw = 144;    // LDS dwords per staged superblock and token
+constexpr int kXsPerSb = 16;  // LDS floats of x sums per staged superblock and token
 
 template <int T>
 __device__ __forceinline__ int xpad(int i) {   // pair index in the chunk -> dword offset
@@ -172,10 +173,11 @@ __device__ __forceinline__ void compute_kq(bool q5, const RawKq &R, int c, const
 }
 
 // Q6_K superblock update of one lane: half s = c >> 1, positions 16h..16h+15
-// (h = c & 1) of the four 32-weight groups of that half.
+// (h = c & 1) of the four 32-weight groups of that half.  xs0 holds, per
+// 16-position half of each sub-block, the dot2 chain of x alone.
 template <int NT>
-__device__ __forceinline__ void compute_q6(const RawQ6 &R, int c, const uint32_t *xw0,
-                                           int tstride_w, int n, float (&acc)[NT]) {
+__device__ __forceinline__ void compute_q6(const RawQ6 &R, int c, const uint32_t *xw0, const float *xs0,
+                                           int tstride_w, int tstride_s, int n, float (&acc)[NT]) {
     const int s = c >> 1, h = c & 1;
     const uint32_t sel = R.mis ? kSelMis : kSelAligned;
     const uint32_t av[5] = {R.a.x, R.a.y, R.a.z, R.a.w, R.a4};
@@ -195,6 +197,7 @@ __device__ __forceinline__ void compute_q6(const RawQ6 &R, int c, const uint32_t
         if (t < n) {
             // x pairs of group g start at position 128s + 32g + 16h (padded).
             const uint32_t *xt = xw0 + t * tstride_w + 68 * s + 8 * h;
+            const float *xh = xs0 + t * tstride_s + 8 * s + h;   // half h of sub-block 4s + g
             float a = acc[t];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -209,7 +212,7 @@ __device__ __forceinline__ void compute_q6(const RawQ6 &R, int c, const uint32_t
                 sg = dot2(oc[2].v[g][1], x1.y, sg);
                 sg = dot2(oc[3].v[g][0], x1.z, sg);
                 sg = dot2(oc[3].v[g][1], x1.w, sg);
-                a = __builtin_fmaf(coef[g], sg, a);
+                a = __builtin_fmaf(coef[g], __builtin_fmaf(g < 2 ? -1056.0f : -384.0f, xh[2 * g], sg), a);
             }
             acc[t] = a;
         }
@@ -294,8 +297,8 @@ struct Pol<T_Q6_K> {
     }
     template <int NT>
     static __device__ __forceinline__ void update(const Raw &R, int c, const KqLane &, const uint32_t *xw0,
-                                                  const float *, int tw, int, int n, float (&acc)[NT]) {
-        compute_q6<NT>(R, c, xw0, tw, n, acc);
+                                                  const float *xs0, int tw, int ts, int n, float (&acc)[NT]) {
+        compute_q6<NT>(R, c, xw0, xs0, tw, ts, n, acc);
     }
 };
 
@@ -351,19 +354,27 @@ __device__ __forceinline__ void x_fetch(const GemvArgs &A, int cb0, int cb1, XPr
     }
 }
 
-// Per-sub-block sums of x by the same dot2 chain the quant sums use (so an
-// all-zero sub-block of quants cancels exactly against its bias).
+// Sums of x by the same dot2 chain the quant sums use (so an all-zero run of
+// quants cancels exactly against its bias): per 32-position sub-block for
+// Q4_K/Q5_K/NVFP4 (16 pairs), per 16-position half sub-block for Q6_K (8 pairs).
+template <int T>
+struct XSum {
+    static constexpr int kPairs = T == T_Q6_K ? 8 : 16;      // pairs per sum
+    static constexpr int kPerSb = T == T_Q6_K ? 16 : 8;      // sums per superblock
+};
+
 template <int T, int NT>
 __device__ __forceinline__ void x_sums(const GemvArgs &A, uint32_t *xw, float *xsum, int cl) {
-    const int tw = A.kc * kSbDw, ts = A.kc * 8;
-    for (int i = threadIdx.x; i < A.n * cl * 8; i += 256) {
-        int t, sb;
-        tok_split<NT>(i, cl * 8, t, sb);
-        const uint32_t *src = xw + t * tw + xpad<T>(sb * 16);
+    constexpr int np = XSum<T>::kPairs, ns = XSum<T>::kPerSb;
+    const int tw = A.kc * kSbDw, ts = A.kc * kXsPerSb;
+    for (int i = threadIdx.x; i < A.n * cl * ns; i += 256) {
+        int t, k;
+        tok_split<NT>(i, cl * ns, t, k);
+        const uint32_t *src = xw + t * tw + xpad<T>(k * np);
         float s = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) s = dot2(0x3C003C00u, src[q], s);
-        xsum[t * ts + sb] = s;
+        for (int q = 0; q < np; ++q) s = dot2(0x3C003C00u, src[q], s);
+        xsum[t * ts + (k / ns) * kXsPerSb + (k % ns)] = s;
     }
 }
 
@@ -429,7 +440,7 @@ __device__ __forceinline__ void chunk_rows(const GemvArgs &A, const Seg &S, int6
     for (int u = 0; u < D; ++u)
         if (b + u * P < cb1) cur[u] = Po::load(S, r, b + u * P, c);
     if (do_stage && early) x_commit<T, NT>(A, xp, xw, xsum, cb0, cb1);
-    const int tw = A.kc * kSbDw, ts = A.kc * 8;
+    const int tw = A.kc * kSbDw, ts = A.kc * kXsPerSb;
     while (b < cb1) {
         const int bn = b + D * P;
         Raw nxt[PF ? D : 1];
@@ -442,7 +453,7 @@ __device__ __forceinline__ void chunk_rows(const GemvArgs &A, const Seg &S, int6
         for (int u = 0; u < D; ++u) {
             const int rb = b + u * P - cb0;
             if (b + u * P < cb1)
-                Po::template update<NT>(cur[u], c, L, xw + rb * kSbDw, xsum + rb * 8, tw, ts, A.n, acc);
+                Po::template update<NT>(cur[u], c, L, xw + rb * kSbDw, xsum + rb * kXsPerSb, tw, ts, A.n, acc);
         }
         if (PF) {
 #pragma unroll
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs A) {
     extern __shared__ uint4 lds[];
     const int kc = A.kc;
     uint32_t *xw = reinterpret_cast<uint32_t *>(lds);                 // [n][kc*144] padded pairs
-    float *xsum = reinterpret_cast<float *>(xw + A.n * kc * kSbDw);   // [n][kc*8]
+    float *xsum = reinterpret_cast<float *>(xw + A.n * kc * kSbDw);   // [n][kc*kXsPerSb]
 
     // The matrix this workgroup serves (selected without indexing the argument
     // array, which would force it into scratch memory).
@@ -612,8 +623,8 @@ __device__ __forceinline__ void gemv1_body(const GemvArgs &A, const Seg &S, int6
     for (int u = 0; u < D; ++u) {
         const int b = p + u * P;
         if (active && b < nb) {
-            Po::template update<1>(cur[u], c, L, xw + b * kSbDw, xsum + b * 8, 0, 0, 1, a1);
-            if (SW) Po::template update<1>(cur2[u], c, L, xw + b * kSbDw, xsum + b * 8, 0, 0, 1, a2);
+            Po::template update<1>(cur[u], c, L, xw + b * kSbDw, xsum + b * kXsPerSb, 0, 0, 1, a1);
+            if (SW) Po::template update<1>(cur2[u], c, L, xw + b * kSbDw, xsum + b * kXsPerSb, 0, 0, 1, a2);
         }
     }
     acc = a1[0];
