@@ -178,6 +178,49 @@ def time_layer(layers, n, steps, warmup):
     return out
 
 
+PREFILL = (("q4k_9728x2560", 12, 9728, 2560), ("q6k_2560x9728", 14, 2560, 9728), ("q5k_4096x2560", 13, 4096, 2560))
+PREFILL_N = 512
+PREFILL_COPIES = 4
+
+
+def time_prefill(reps=10):
+    """Prefill chunk of 512 tokens through the MFMA GEMM on the three config
+    shapes (4 rotated copies of each weight), from a HIP graph."""
+    import torch
+    import gemm_q4_q5_amd as qg
+    import synth
+    ws = []
+    for i, (name, wt, m, k) in enumerate(PREFILL):
+        data, scales = synth.weights(wt, m, k, synth.rng_for(3, i))
+        base = qg.QWeight.from_host(wt, data, m, k, scales, device="cuda")
+        ws.append([base] + [qg.QWeight(wt, base.data.clone(), m, k, None) for _ in range(PREFILL_COPIES - 1)])
+    rng = synth.rng_for(3, 99)
+    xs = {k: torch.from_numpy(synth.activations(PREFILL_N, k, rng)).to("cuda") for k in (2560, 9728)}
+    ys = [torch.empty((PREFILL_N, m), dtype=torch.float32, device="cuda") for _, _, m, _ in PREFILL]
+
+    def calls(only=None):
+        for c in range(PREFILL_COPIES):
+            for i, (name, wt, m, k) in enumerate(PREFILL):
+                if only is None or only == i:
+                    qg.qgemm_prefill(ws[i][c], xs[k], ys[i])
+
+    calls()
+    torch.cuda.synchronize()
+    out = {}
+    flops_all = sum(2.0 * PREFILL_N * m * k for _, _, m, k in PREFILL)
+    for only in (None, 0, 1, 2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls(only)
+        ms = _time_graph(g, reps, 2) / (reps * PREFILL_COPIES)
+        fl = flops_all if only is None else 2.0 * PREFILL_N * PREFILL[only][2] * PREFILL[only][3]
+        key = "all" if only is None else PREFILL[only][0]
+        out[key] = {"us": round(ms * 1000, 2), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                    "pct_of_2.5PF": round(100 * fl / (ms * 1e-3) / 2.5e15, 2)}
+        del g
+    return out
+
+
 def cpu_baseline(target_s=10.0):
     """The CPU oracle on the same layer at N=1, repeated to ~target_s of work."""
     import oracle
@@ -219,6 +262,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=72)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-n32", action="store_true", help="skip the N=32 pass")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-GEMM pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel", choices=KERNELS, default=None,
                     help="profile mode: replay only this call over the 36-layer rotation")
@@ -288,6 +332,8 @@ def main():
         if "kernel_us" in r32:
             res["n32"]["kernels"] = {k: {"us": round(v, 3), "GB/s": round(b32[k] / (v * 1e3), 1)}
                                      for k, v in r32["kernel_us"].items()}
+    if not args.no_prefill:
+        res["prefill_n512"] = time_prefill()
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res))

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
             "qgemv_pair": ([W, W, p, fp, fp, i32, p], ctypes.c_int),
             "qgemv_triple": ([W, W, W, p, fp, fp, fp, i32, p], ctypes.c_int),
             "qgemv_pair_swiglu": ([W, W, p, fp, i32, p], ctypes.c_int),
+            "qgemm_prefill": ([W, p, fp, i64, p], ctypes.c_int),
             "qdequant": ([W, fp, p], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -189,6 +190,15 @@ def qgemv_pair_swiglu(wg: QWeight, wu: QWeight, x, h=None):
     cg, cu = wg.c(), wu.c()
     _check(lib().qgemv_pair_swiglu(ctypes.byref(cg), ctypes.byref(cu), _ptr(x), _ptr(h), n, _stream()))
     return h
+
+
+def qgemm_prefill(w: QWeight, x, y=None):
+    """MFMA prefill GEMM: y[n, m] = x[n, k] . W^T for any n >= 1."""
+    n = _rows(x)
+    y = _out((n, w.m), x, y)
+    cw = w.c()
+    _check(lib().qgemm_prefill(ctypes.byref(cw), _ptr(x), _ptr(y), n, _stream()))
+    return y
 
 
 def qdequant(w: QWeight, out=None):

@@ -16,6 +16,7 @@
 
 #include "qgemm.h"
 #include "qg_kernels.h"
+#include "qg_prefill.h"
 
 namespace {
 
@@ -289,6 +290,38 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, f
     const qg_weight *ws[2] = {wg, wu};
     float *ys[2] = {h, h};
     return run_gemv(ws, ys, nullptr, 2, x, n, qg::MODE_SWIGLU, stream);
+}
+
+int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *stream) {
+    int rc;
+    if ((rc = check_weight(w, "w")) || (rc = check_x(x)) || (rc = check_y(y, "y"))) return rc;
+    if (n < 1 || n > ((int64_t)1 << 30)) return fail(QG_ERR_SHAPE, "n = %lld out of range", (long long)n);
+    qg::PrefillArgs a;
+    memset(&a, 0, sizeof a);
+    a.data = (const uint8_t *)w->data;
+    a.scales = (const uint8_t *)w->scales;
+    a.x = x;
+    a.y = y;
+    a.row_bytes = qg_row_bytes(w->type, w->k);
+    a.m = w->m;
+    a.n = n;
+    a.k = (int32_t)w->k;
+    a.type = w->type;
+    // Largest tile that still gives about two workgroups per CU (512 on 256 CUs).
+    int bm = 64, bn = 64;
+    const int tiles[3][2] = {{128, 128}, {128, 64}, {64, 64}};
+    for (auto &t : tiles) {
+        const int64_t wgs = ((w->m + t[1] - 1) / t[1]) * ((n + t[0] - 1) / t[0]);
+        if (wgs >= 512) {
+            bm = t[0];
+            bn = t[1];
+            break;
+        }
+    }
+    hipError_t e = qg::launch_prefill(a, bm, bn, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+    g_err.clear();
+    return QG_OK;
 }
 
 int qdequant(const qg_weight *w, float *out, void *stream) {

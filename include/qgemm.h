@@ -166,6 +166,18 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
                       float *h, int32_t n, void *stream);
 
 /*
+ * Prefill-chunk GEMM on the matrix cores ([PF] Path E / E5: tensor-core K-quant
+ * prefill GEMM with scales decoded once per (row, sub-block) and one dequantized
+ * weight tile shared by all waves of a block): Y[n][m] = X[n][k] W^T for any
+ * n >= 1 and every weight type.  Each workgroup dequantizes its weight tile once
+ * into fp16 in LDS (one rounding of the exact fp32 weight, |error| <= 2^-11 |w|)
+ * and multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
+ * y fp32 [n][m].  Deterministic; no row-invariance contract ([TK] "Prefill
+ * kernels": chunk kernels share work across rows and are checked by agreement).
+ */
+int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *stream);
+
+/*
  * Decoder probe: out[r][k] = the fp32 weight value of row r, column k, for every
  * element (the device decoders the products use).  out fp32 [m][k].
  */
