@@ -244,6 +244,61 @@ def cpu_baseline(target_s=10.0):
                       f"oracle = plain C dequant + fp64 dot, OpenMP over rows"}
 
 
+CAL_BYTES = 1 << 30   # bytes read (and written) by one calibration copy
+
+
+def calibration_copy(reps=3):
+    """A plain elementwise copy of known size (torch.neg over 1 GiB of fp32, so
+    1 GiB read and 1 GiB written, cold), run inside a counter-collection run
+    beside the kernel: the ratio of what FETCH_SIZE / WRITE_SIZE report for it
+    to its known byte counts scales the kernel's counters to bytes."""
+    import torch
+    bufs = [torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda") for _ in range(2 * reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        torch.neg(bufs[2 * i], out=bufs[2 * i + 1])
+    torch.cuda.synchronize()
+    del bufs
+
+
+def _counter_means(path, counter):
+    """{kernel name: [per-dispatch values]} for one counter of a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def pmc_summary(kernel, fetch_csv, write_csv):
+    """Turn two counter runs of `bench.py --kernel K` (FETCH_SIZE, then WRITE_SIZE)
+    into HBM bytes per launch of K's kernel, scaled by the calibration copy, and
+    store them in profiles/traffic_<K>.json keyed by the kernel sources' hash."""
+    res = {"kernel_call": kernel, "kernel_source_sha": kernel_source_sha()}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = _counter_means(path, counter)
+        qg = {k: v for k, v in vals.items() if "qg::" in k}
+        name = max(qg, key=lambda k: len(qg[k]))   # the kernel the graph replays
+        cal = [v for k, vs in vals.items() if "neg" in k for v in vs]
+        kib = float(np.median(qg[name]))
+        cal_kib = float(np.median(cal))
+        scale = (CAL_BYTES / 1024.0) / cal_kib
+        res[counter] = {"kernel": name, "dispatches": len(qg[name]), "kib_per_dispatch": round(kib, 1),
+                        "calibration_kib": round(cal_kib, 1), "scale": round(scale, 4),
+                        "bytes_per_launch": round(kib * 1024.0 * scale)}
+        total += kib * 1024.0 * scale
+    res["bytes_per_launch"] = round(total)
+    res["algorithmic_bytes"] = layer_call_bytes(1)[kernel]
+    out = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
+
+
 def load_traffic(sha):
     p = os.path.join(ROOT, "profiles", "traffic_pair.json")
     if not os.path.exists(p):
@@ -267,7 +322,14 @@ def main():
     ap.add_argument("--kernel", choices=KERNELS, default=None,
                     help="profile mode: replay only this call over the 36-layer rotation")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per call in --kernel mode")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="--kernel mode: also run the known-size copy that scales HBM counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two counter runs of --kernel K into profiles/traffic_K.json")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.kernel or "pair", *args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the product is a single-GPU kernel library)", file=sys.stderr)
@@ -289,6 +351,8 @@ def main():
         ms = _time_graph(gk, reps, max(1, args.warmup // LAYERS))
         us = 1000.0 * ms / (reps * LAYERS)
         b = layer_call_bytes(n)[args.kernel]
+        if args.calibrate:
+            calibration_copy()
         print(json.dumps({"kernel": args.kernel, "tokens": n, "launches": reps * LAYERS,
                           "us_per_launch": round(us, 3), "GB/s": round(b / (us * 1e3), 1),
                           "algorithmic_bytes": b}))
