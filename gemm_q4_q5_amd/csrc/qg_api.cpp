@@ -17,6 +17,7 @@
 #include "qgemm.h"
 #include "qg_kernels.h"
 #include "qg_prefill.h"
+#include "qg_mma_launch.h"
 
 namespace {
 
@@ -85,50 +86,57 @@ int check_rows(int32_t n) {
     return QG_OK;
 }
 
-// Lanes per weight row = 4 * P, a pure function of the weight's shape.  A
-// single-token call is bound by memory-level parallelism: P grows until the
-// matrix alone yields about two wavefronts per SIMD (2048 on 256 CUs) or
-// until a lane would be left with less than one superblock, and at least until
-// one lane's share of a row fits one round of loads.
-int choose_p(int32_t type, int64_t m, int64_t k) {
+// Waves splitting K for one row tile of 16 rows: a pure function of (type, m, k),
+// so a row's partial sums -- and its bits -- never depend on n or on the other
+// matrices of a launch.  Doubles (up to 16, while every wave keeps a superblock)
+// until each wave's superblocks fit one round of loads in flight (kMmaDepth) and
+// the matrix yields at least 256 waves.
+int choose_ks(int32_t type, int64_t m, int64_t k) {
     (void)type;
-    const int64_t nb = k / 256;
-    int p = 1;
-    while (p < qg::kMaxP && (nb + p - 1) / p > qg::kDepth1) p *= 2;
-    while (p < qg::kMaxP && m * p / 16 < 2048 && nb >= 2 * p) p *= 2;
-    return p;
+    const int64_t tiles = (m + 15) / 16, nb = k / 256;
+    int ks = 1;
+    while (ks < 16 && 2 * ks <= nb && ((nb + ks - 1) / ks > qg::kMmaDepth || tiles * ks < 256)) ks *= 2;
+    return ks;
 }
 
-int log2i(int v) {
-    int l = 0;
-    while ((1 << l) < v) ++l;
-    return l;
-}
+constexpr size_t kMmaLdsBudget = 65536;
+constexpr size_t kMmaBytesPerTokSb = 4 * 9 * 16;   // staged x per token and superblock (units of 16 B)
+constexpr size_t kMmaZeroBytes = 9 * 16;
 
-constexpr int kWaves = 4;            // wavefronts per workgroup
-constexpr size_t kLdsBudget = 65536;
-
-int bucket(int n) {
-    int b = 1;
-    while (b < n) b *= 2;
-    return b;
-}
-
-// Assemble and launch one gemv_kernel call over `nseg` matrices sharing x.
-int run_gemv(const qg_weight *const *w, float *const *y, const float *resid, int nseg, const void *x,
-             int32_t n, int mode, void *stream) {
-    qg::GemvArgs a;
+// Assemble and launch one MFMA-path call over `nseg` matrices sharing x
+// (SwiGLU: w[0] gate and w[1] up, served by the same lanes).
+int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int nseg, const void *x, int32_t n,
+            int mode, void *stream) {
+    qg::MmaArgs a;
     memset(&a, 0, sizeof a);
     const int64_t k = w[0]->k;
+    const bool sw = mode == qg::MODE_SWIGLU;
+    // Two matrices of one shape and type (SwiGLU, or a gate/up pair above 16
+    // tokens) are served by the same waves, one tile of each per wave, sharing the
+    // x operands.
+    const bool fuse2 = sw || (n > 16 && nseg == 2 && w[0]->type == w[1]->type && w[0]->m == w[1]->m);
     a.x = x;
-    a.nseg = mode == qg::MODE_SWIGLU ? 2 : nseg;
+    a.nseg = fuse2 ? 1 : nseg;
     a.k = (int32_t)k;
     a.nb = (int32_t)(k / 256);
     a.n = n;
     a.mode = mode;
-    int grid = 0, pmax = 1;
-    for (int s = 0; s < nseg; ++s) {
-        qg::Seg &g = a.seg[s];
+    a.nt = fuse2 ? 2 : 1;
+    // Workgroups of at least four waves; KS waves per row tile.
+    int wv = 4;
+    int ks[3] = {1, 1, 1};
+    for (int s = 0; s < a.nseg; ++s) {
+        ks[s] = choose_ks(w[s]->type, w[s]->m, k);
+        wv = std::max(wv, ks[s]);
+    }
+    if (!sw && a.nt == 2 && wv > 8) {   // a plain pair takes two tiles per wave only up to 8 waves
+        a.nt = 1;
+        a.nseg = 2;
+    }
+    a.wv = wv;
+    int grid = 0;
+    for (int s = 0; s < a.nseg; ++s) {
+        qg::MSeg &g = a.seg[s];
         g.data = (const uint8_t *)w[s]->data;
         g.scales = (const uint8_t *)w[s]->scales;
         g.y = y[s];
@@ -136,47 +144,37 @@ int run_gemv(const qg_weight *const *w, float *const *y, const float *resid, int
         g.row_bytes = qg_row_bytes(w[s]->type, k);
         g.type = w[s]->type;
         g.m = (int32_t)w[s]->m;
-        g.P = choose_p(w[s]->type, w[s]->m, k);
-        g.lp = log2i(g.P);
-        pmax = std::max(pmax, g.P);
-        const int64_t rows_per_wg = kWaves * (16 / g.P);
-        const bool counted = !(mode == qg::MODE_SWIGLU && s == 1);   // swiglu: seg 1 rides on seg 0's lanes
-        g.wg_begin = counted ? grid : a.seg[0].wg_begin;
-        if (counted) grid += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
+        g.ks = ks[s];
+        g.wg_begin = grid;
+        if (a.nt == 2) {
+            g.data2 = (const uint8_t *)w[1]->data;
+            g.scales2 = (const uint8_t *)w[1]->scales;
+            g.y2 = sw ? nullptr : y[1];
+        }
+        const int64_t rows_per_wg = 16 * (wv / ks[s]);
+        grid += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
     }
-    if (mode == qg::MODE_SWIGLU) {
-        a.seg[1].wg_begin = 1 << 30;   // never selected by blockIdx
-        a.seg[1].y = y[0];
+    const int ng = n > 16 ? 2 : 1;
+    const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
+    const int kc = (int)std::max<size_t>(1, (kMmaLdsBudget - kMmaZeroBytes) / per_sb);
+    a.kc = std::min(kc, a.nb);
+    size_t lds = kMmaZeroBytes + per_sb * a.kc;
+    // Decode path (each wave stages its own x) where a wave's superblocks fit one
+    // round of loads and their x one staging half-group per lane.
+    const int depth = a.nt == 2 ? 2 : qg::kMmaDepth;
+    for (int s = 0; s < a.nseg; ++s) {
+        const int maxcnt = (a.nb + ks[s] - 1) / ks[s];
+        const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
+        if (maxcnt <= depth && 8 * n * maxcnt <= 64 * qg::kMmaDecRounds && need <= kMmaLdsBudget) {
+            a.seg[s].dec = 1;
+            lds = std::max(lds, need);
+        }
     }
-    // Superblocks of x staged per LDS chunk: the whole row when it fits, else
-    // as many as the budget allows, rounded down to a multiple of P when that
-    // leaves at least P (the chunking never changes a lane's order of work).
-    const size_t per_sb = (size_t)n * (144 * 4 + 16 * 4);   // padded x pairs + x sums
-    int kc = (int)std::max<size_t>(1, kLdsBudget / per_sb);
-    if (kc >= a.nb)
-        kc = a.nb;
-    else if (kc >= pmax)
-        kc = kc / pmax * pmax;
-    a.kc = kc;
-    const size_t lds = per_sb * kc;
+    const size_t part = (size_t)wv * 64 * 4 * (4 * ng * a.nt);   // partial sums of the K split
+    lds = std::max(lds, part);
     int ts = 0;
     for (int s = 0; s < nseg; ++s) ts |= qg::type_bit(w[s]->type);
-    const int nt = bucket(n);
-    // The single-token kernel stages all of x at once (up to 64 superblocks);
-    // longer rows run the multi-token kernel with n = 1 (same per-row
-    // arithmetic, chunked staging).
-    // Slots per lane: the largest share of a row any matrix of the launch gives
-    // one lane (the single-token kernel holds them all in flight at once).
-    int depth = 1;
-    for (int s = 0; s < nseg; ++s) depth = std::max(depth, (a.nb + a.seg[s].P - 1) / a.seg[s].P);
-    const bool one = nt == 1 && a.nb <= qg::kMaxNb1 && depth <= qg::kDepth1;
-    hipError_t e;
-    if (one)
-        e = depth == 1   ? qg::launch_gemv1_d1(a, ts, grid, lds, (hipStream_t)stream)
-            : depth == 2 ? qg::launch_gemv1_d2(a, ts, grid, lds, (hipStream_t)stream)
-                         : qg::launch_gemv1_d3(a, ts, grid, lds, (hipStream_t)stream);
-    else
-        e = qg::launch_gemv_ntn(a, nt == 1 ? 2 : nt, grid, lds, (hipStream_t)stream);
+    hipError_t e = qg::launch_mma(a, ts, grid, lds, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
     g_err.clear();
     return QG_OK;
@@ -189,7 +187,7 @@ int gemv_single(int32_t type, const void *wdata, const void *scales, const void 
     if ((rc = check_weight(&w, "w")) || (rc = check_x(x)) || (rc = check_y(y, "y"))) return rc;
     const qg_weight *ws[1] = {&w};
     float *ys[1] = {y};
-    return run_gemv(ws, ys, nullptr, 1, x, 1, qg::MODE_PLAIN, stream);
+    return run_mma(ws, ys, nullptr, 1, x, 1, qg::MODE_PLAIN, stream);
 }
 
 }  // namespace
@@ -241,7 +239,7 @@ int qgemm_rows(const qg_weight *w, const void *x, float *y, int32_t n, void *str
     if ((rc = check_weight(w, "w")) || (rc = check_x(x)) || (rc = check_y(y, "y")) || (rc = check_rows(n)))
         return rc;
     float *ys[1] = {y};
-    return run_gemv(&w, ys, nullptr, 1, x, n, qg::MODE_PLAIN, stream);
+    return run_mma(&w, ys, nullptr, 1, x, n, qg::MODE_PLAIN, stream);
 }
 
 int qgemv_add(const qg_weight *w, const void *x, const float *resid, float *y, int32_t n, void *stream) {
@@ -250,7 +248,7 @@ int qgemv_add(const qg_weight *w, const void *x, const float *resid, float *y, i
         (rc = check_y(resid, "resid")) || (rc = check_rows(n)))
         return rc;
     float *ys[1] = {y};
-    return run_gemv(&w, ys, resid, 1, x, n, qg::MODE_PLAIN, stream);
+    return run_mma(&w, ys, resid, 1, x, n, qg::MODE_PLAIN, stream);
 }
 
 int qgemv_pair(const qg_weight *w0, const qg_weight *w1, const void *x, float *y0, float *y1, int32_t n,
@@ -262,7 +260,7 @@ int qgemv_pair(const qg_weight *w0, const qg_weight *w1, const void *x, float *y
     if (w0->k != w1->k) return fail(QG_ERR_SHAPE, "pair: k differs (%lld vs %lld)", (long long)w0->k, (long long)w1->k);
     const qg_weight *ws[2] = {w0, w1};
     float *ys[2] = {y0, y1};
-    return run_gemv(ws, ys, nullptr, 2, x, n, qg::MODE_PLAIN, stream);
+    return run_mma(ws, ys, nullptr, 2, x, n, qg::MODE_PLAIN, stream);
 }
 
 int qgemv_triple(const qg_weight *w0, const qg_weight *w1, const qg_weight *w2, const void *x, float *y0,
@@ -275,7 +273,7 @@ int qgemv_triple(const qg_weight *w0, const qg_weight *w1, const qg_weight *w2, 
     if (w0->k != w1->k || w0->k != w2->k) return fail(QG_ERR_SHAPE, "triple: k differs between the weights");
     const qg_weight *ws[3] = {w0, w1, w2};
     float *ys[3] = {y0, y1, y2};
-    return run_gemv(ws, ys, nullptr, 3, x, n, qg::MODE_PLAIN, stream);
+    return run_mma(ws, ys, nullptr, 3, x, n, qg::MODE_PLAIN, stream);
 }
 
 int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, float *h, int32_t n,
@@ -289,7 +287,7 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, f
     if (wg->type != wu->type) return fail(QG_ERR_TYPE, "swiglu pair: gate and up must have the same type");
     const qg_weight *ws[2] = {wg, wu};
     float *ys[2] = {h, h};
-    return run_gemv(ws, ys, nullptr, 2, x, n, qg::MODE_SWIGLU, stream);
+    return run_mma(ws, ys, nullptr, 2, x, n, qg::MODE_SWIGLU, stream);
 }
 
 int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *stream) {

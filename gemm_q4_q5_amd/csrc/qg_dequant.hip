@@ -1,6 +1,6 @@
 // Dequant probe (gfx950): writes every weight of a matrix as fp32 through the
 // same loads and decoders the products use.
-#include "qg_gemv.hpp"
+#include "qg_loads.hpp"
 
 namespace qg {
 

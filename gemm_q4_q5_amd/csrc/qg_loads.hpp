@@ -1,0 +1,139 @@
+// Per-lane raw loads of one 64-weight chunk of a quantized superblock, shared by the
+// dequant probe (qg_dequant.hip) and the dequantizing stage of the prefill GEMM
+// (qg_prefill.hip).  Chunk c of a K-quant superblock is quant bytes 32c .. 32c+31
+// (sub-blocks 2c and 2c+1); for Q6_K it is half c >> 1, positions 16(c & 1) ..
+// 16(c & 1)+15 of each of its four 32-weight groups; for NVFP4, codes 64c .. 64c+63.
+#pragma once
+#include "qg_device.hpp"
+#include "qg_kernels.h"
+
+namespace qg {
+
+// ---------------------------------------------------------------------------
+// Raw per-lane loads of one superblock, one struct per type, kept separate from
+// the arithmetic so a lane can have several superblocks in flight.
+struct RawKq {
+    uint4 hdr, q0, q1, h0, h1;
+};
+struct RawQ6 {
+    uint4 a, b, h;
+    uint32_t a4, b4, h4;
+    uint2 s01;
+    uint32_t s2;
+    uint32_t d;
+    uint32_t mis;
+};
+struct RawF4 {
+    uint4 q0, q1;
+    uint32_t sc;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Weight loads.  Ordinary (temporal) loads on purpose: a lane's two 16-byte
+// quant loads and its header load hit the same 128-byte lines, which must stay
+// in the vector L1 between the instructions; non-temporal loads made every
+// second access go back to L2.
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8(const uint8_t *p) {
+    const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+__device__ __forceinline__ RawKq load_kq(bool q5, const uint8_t *blk, int c) {
+    RawKq r;
+    r.hdr = ld16(blk);
+    if (q5) {
+        r.h0 = ld16(blk + 16);
+        r.h1 = ld16(blk + 32);
+        r.q0 = ld16(blk + 48 + 32 * c);
+        r.q1 = ld16(blk + 64 + 32 * c);
+    } else {
+        r.h0 = r.h1 = make_uint4(0, 0, 0, 0);
+        r.q0 = ld16(blk + 16 + 32 * c);
+        r.q1 = ld16(blk + 32 + 32 * c);
+    }
+    return r;
+}
+
+// Q6_K blocks sit at 210-byte offsets, so a block may start 2 bytes past a
+// 4-byte boundary.  Every load is issued from the 4-byte-aligned address below
+// the data, with one extra dword that the byte-pairing permute uses to realign;
+// the extra dword is always inside the same block.
+__device__ __forceinline__ RawQ6 load_q6(const uint8_t *blk, int c) {
+    const int s = c >> 1, h = c & 1;
+    const uint32_t mis = (uint32_t)((uintptr_t)blk & 3u);   // 0 or 2
+    const uint8_t *base = blk - mis;
+    RawQ6 r;
+    r.mis = mis;
+    const uint8_t *pa = base + 64 * s + 16 * h;
+    const uint8_t *pb = pa + 32;
+    const uint8_t *ph = base + 128 + 32 * s + 16 * h;
+    r.a = ld16(pa);
+    r.b = ld16(pb);
+    r.h = ld16(ph);
+    r.a4 = ld4(mis ? pa + 16 : pa + 12);
+    r.b4 = ld4(mis ? pb + 16 : pb + 12);
+    r.h4 = ld4(mis ? ph + 16 : ph + 12);
+    const uint8_t *ps = base + 192 + 8 * s;
+    r.s01 = ld8(ps);
+    r.s2 = ld4(mis ? ps + 8 : ps + 4);
+    r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+    return r;
+}
+
+__device__ __forceinline__ RawF4 load_f4(const uint8_t *codes, const uint8_t *scales, int c) {
+    RawF4 r;
+    r.q0 = ld16(codes + 32 * c);
+    r.q1 = ld16(codes + 32 * c + 16);
+    r.sc = ld4(scales + 4 * c);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// The raw chunk type and loader of a weight type.
+template <int T>
+struct Loader;
+
+template <>
+struct Loader<T_Q4_K> {
+    typedef RawKq Raw;
+    static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
+                                               int b, int c) {
+        return load_kq(false, data + r * row_bytes + (int64_t)b * 144, c);
+    }
+};
+
+template <>
+struct Loader<T_Q5_K> {
+    typedef RawKq Raw;
+    static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
+                                               int b, int c) {
+        return load_kq(true, data + r * row_bytes + (int64_t)b * 176, c);
+    }
+};
+
+template <>
+struct Loader<T_Q6_K> {
+    typedef RawQ6 Raw;
+    static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
+                                               int b, int c) {
+        return load_q6(data + r * row_bytes + (int64_t)b * 210, c);
+    }
+};
+
+template <>
+struct Loader<T_NVFP4> {
+    typedef RawF4 Raw;
+    static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *scales, int64_t row_bytes,
+                                               int64_t r, int b, int c) {
+        return load_f4(data + r * row_bytes + (int64_t)b * 128, scales + r * (row_bytes / 8) + (int64_t)b * 16, c);
+    }
+};
+
+}  // namespace qg

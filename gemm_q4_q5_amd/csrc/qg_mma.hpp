@@ -1,0 +1,726 @@
+// Row-invariant weight-streaming product on the matrix cores (gfx950), for
+// 1 <= n <= 32 tokens: y[t][r] = sum_k w[r][k] * x[t][k].
+//
+// Sources: reflex-llm kernel notes (fused K-quant GEMV; batched GEMM: weights
+// streamed once for all tokens, y[token*M + row]); TandemLLM Kernels page ("Row
+// invariance", "Verify twins", and "NVFP4 matrix products": weights are one operand
+// and activations the other operand of the matrix instruction, decoded straight from
+// wide loads into operand registers, so 1..16 rows cost one instruction per weight
+// tile and 17..32 rows two).
+//
+// Work split.  A wave owns a tile of 16 weight rows and every KS-th superblock of
+// K (superblocks kp, kp + KS, ...); the KS waves of a tile sit in one workgroup and
+// their partial sums are added in wave order.  KS depends only on (type, m, k).
+// v_mfma_f32_16x16x32_f16 takes
+//   A = x          16 tokens x 32 k   (lane (t, g): token t = lane & 15, k-slots 8g..8g+7)
+//   B = W^T        32 k x 16 rows     (lane (j, g): row j = lane & 15, the same k-slots)
+//   D[t][j]        lane (j, g) holds tokens 4g .. 4g+3 of row j.
+// Lane (j, g) streams chunk g (weights 64g .. 64g+63) of each of its superblocks of
+// row j.  The k-slot order inside a step follows the cheapest unpacking of the
+// weights; x is staged in LDS in that same order, so no weight needs a permute.
+//
+// Load order (decode: the whole layer's weights are one cold stream).  Every wave
+// issues the loads of the x its superblocks need, then all of its weight loads (up
+// to kDepth superblocks; a ring refills behind the computation when a wave has
+// more), then writes x to a region of LDS of its own.  Nothing ties a wave's
+// start of computation to the other waves: issuing stalls once the memory
+// pipeline is full, and a workgroup barrier after the loads, or x staged by some
+// waves for all, held whole workgroups until their slowest wave had its data.
+//
+// Exact operands.  K-quants: the weight operand is sc*q (Q4_K/Q5_K: at most
+// 63*31 = 1953, exact in fp16) and the superblock factors are applied in fp32 after
+// the MFMAs of the superblock:
+//     y += d * sum_k sc*q*x  -  dmin * sum_k m*x
+// the second sum being a second MFMA chain over the same x operands, with the
+// sub-block's min (at most 63, exact) as the weight operand.
+// Q6_K: the operand is sc*(q-32), exact whenever |sc*(q-32)| <= 2048 (every
+// |sc| <= 64, which covers int8 scales drawn in 0..63), otherwise rounded once to
+// fp16 (relative error <= 2^-11); d is applied in fp32.  NVFP4: e2m1 * e4m3 is exact
+// in fp16 and the MFMA accumulates over all of K.
+//
+// Row invariance.  An output (t, r) is produced by the same instructions for every
+// n: its MFMAs see only token t's x (A row t) and row r's weights (B column r);
+// tokens >= n are zero A rows that never mix into other rows; the split of K over
+// waves and the order of the partials are functions of the weight's shape only.
+// The number of token groups (1 for n <= 16, 2 above) only adds instructions for
+// the second group.
+#pragma once
+#include "qg_device.hpp"
+#include "qg_kernels.h"
+#include "qg_mma_launch.h"
+
+namespace qg {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDepth = kMmaDepth;
+
+// ---------------------------------------------------------------------------
+// Raw per-lane loads of one superblock (lane chunk g).  Ordinary (temporal) loads:
+// a lane's header and quant loads hit the same 128-byte lines, which must stay in
+// the vector L1 between the instructions.
+struct MRawKq {
+    uint4 hdr, q0, q1, h0, h1;
+};
+// Q6_K: the three 16-byte runs of the lane's chunk, the dword after each (for
+// re-aligning blocks at 2-byte offsets; taken from neighbouring lanes, see
+// q6_extras), the scale bytes, d and the offset.
+struct MRawQ6 {
+    uint4 a, b, h;
+    uint32_t a4, b4, h4, s2;
+    uint32_t s0, s1, d, mis;
+};
+struct MRawF4 {
+    uint4 q0, q1;
+    uint32_t sc;
+};
+
+__device__ __forceinline__ uint4 mld16(const uint8_t *p) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t mld4(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+template <int T>
+struct MRawOf {
+    typedef MRawKq type;
+};
+template <>
+struct MRawOf<T_Q6_K> {
+    typedef MRawQ6 type;
+};
+template <>
+struct MRawOf<T_NVFP4> {
+    typedef MRawF4 type;
+};
+
+// Q6_K blocks sit at 210-byte offsets, so a block may start 2 bytes past a 4-byte
+// boundary.  Every load is issued from the 4-byte-aligned address below the data;
+// the dword after each run, which the byte-pairing permute needs to realign, is
+// the first dword of another lane's run (q6_extras).
+template <int T>
+__device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, const uint8_t *srow, int b, int g) {
+    typename MRawOf<T>::type r;
+    if constexpr (T == T_Q4_K) {
+        const uint8_t *blk = row + (int64_t)b * 144;
+        r.hdr = mld16(blk);
+        r.q0 = mld16(blk + 16 + 32 * g);
+        r.q1 = mld16(blk + 32 + 32 * g);
+    } else if constexpr (T == T_Q5_K) {
+        const uint8_t *blk = row + (int64_t)b * 176;
+        r.hdr = mld16(blk);
+        r.h0 = mld16(blk + 16);
+        r.h1 = mld16(blk + 32);
+        r.q0 = mld16(blk + 48 + 32 * g);
+        r.q1 = mld16(blk + 64 + 32 * g);
+    } else if constexpr (T == T_Q6_K) {
+        const uint8_t *blk = row + (int64_t)b * 210;
+        const int s = g >> 1, h = g & 1;
+        const uint32_t mis = (uint32_t)((uintptr_t)blk & 3u);   // 0 or 2
+        const uint8_t *base = blk - mis;
+        const uint8_t *pa = base + 64 * s + 16 * h;
+        const uint8_t *pb = pa + 32;
+        const uint8_t *ph = base + 128 + 32 * s + 16 * h;
+        r.mis = mis;
+        r.a = mld16(pa);
+        r.b = mld16(pb);
+        r.h = mld16(ph);
+        const uint8_t *ps = base + 192 + 8 * s;
+        const u32x2 s01 = *reinterpret_cast<const u32x2 *>(ps);
+        r.s0 = s01.x;
+        r.s1 = s01.y;
+        r.s2 = mld4(mis ? ps + 8 : ps + 4);
+        r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+    } else {
+        const uint8_t *c = row + (int64_t)b * 128;
+        r.q0 = mld16(c + 32 * g);
+        r.q1 = mld16(c + 32 * g + 16);
+        r.sc = mld4(srow + (int64_t)b * 16 + 4 * g);
+    }
+    return r;
+}
+
+__device__ __forceinline__ h2 h2c(float v) {
+    const _Float16 h = (_Float16)v;
+    return (h2){h, h};
+}
+// Fused a*b + c on fp16 pairs (one rounding: v_pk_fma_f16).
+__device__ __forceinline__ uint32_t pk_fma(uint32_t a, h2 b, h2 c) {
+    return as_u32(__builtin_elementwise_fma(as_h2(a), b, c));
+}
+__device__ __forceinline__ uint32_t pk_mul(uint32_t a, h2 b) { return as_u32(as_h2(a) * b); }
+
+__device__ __forceinline__ h8 mk_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_bit_cast(h8, (u32x4){a, b, c, d});
+}
+__device__ __forceinline__ h8 u4h8(uint4 v) { return mk_h8(v.x, v.y, v.z, v.w); }
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+// ---------------------------------------------------------------------------
+// x staging.  For token t < n, staged superblock cb and lane group g, eight
+// 16-byte units at
+//     unit ((cb*4 + g)*n + t)*9 + s
+// hold the eight x values of each step s (0..7) in the k-slot order of the weight
+// operand; a ninth unit pads the pitch to 144 bytes, which makes the 16 tokens of
+// a step read conflict-free.
+// Lanes of tokens >= n read a block of zeros at the start of LDS instead (no
+// branch, no exec mask).
+//
+// k-slot order of step s for lane group g (offsets inside the superblock):
+//   Q4_K/Q5_K: 64g + {4s, 4s+2, 4s+1, 4s+3, 32+4s, 34+4s, 33+4s, 35+4s}
+//   Q6_K:      128(g >> 1) + 16(g & 1) + 4(s >> 1) + 64(s & 1) + {0..3, 32..35}
+//   NVFP4:     64g + 8s + 0..7
+constexpr int kUnitsPerTok = 9;
+constexpr int kZeroUnits = 9;
+
+template <int T>
+__device__ __forceinline__ void slot_pieces(int g, int s, int &o0, int &o1) {
+    if constexpr (T == T_Q6_K) {
+        o0 = 128 * (g >> 1) + 16 * (g & 1) + 4 * (s >> 1) + 64 * (s & 1);
+        o1 = o0 + 32;
+    } else if constexpr (T == T_NVFP4) {
+        o0 = 64 * g + 8 * s;
+        o1 = o0 + 4;
+    } else {
+        o0 = 64 * g + 4 * s;
+        o1 = o0 + 32;
+    }
+}
+
+// A staging half-group: the x behind units 4h .. 4h+3 of one (superblock, lane
+// group, token), fetched as four 16-byte loads from one base; half-group index
+// q = ((cb*4 + g)*n + t)*2 + h.
+struct XHalf {
+    uint4 v[4];
+};
+
+// Offset (in halves, from the superblock) of a half-group's base, and where the
+// two 8-byte pieces of its step 4h + i sit among the four loads.
+template <int T>
+__device__ __forceinline__ int xhalf_base(int g, int h) {
+    if constexpr (T == T_Q6_K) return 128 * (g >> 1) + 16 * (g & 1) + 8 * h;
+    else if constexpr (T == T_NVFP4) return 64 * g + 32 * h;
+    else return 64 * g + 16 * h;
+}
+// Loads at base + {0, 8, 32, 40} (Q4_K/Q5_K), {0, 64, 32, 96} (Q6_K), {0, 8, 16, 24} (NVFP4).
+template <int T>
+__device__ __forceinline__ int xhalf_off(int l) {
+    if constexpr (T == T_Q6_K) return (l & 1) * 64 + (l >> 1) * 32;
+    else if constexpr (T == T_NVFP4) return 8 * l;
+    else return (l & 1) * 8 + (l >> 1) * 32;
+}
+template <int T>
+__device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
+    uint4 v;
+    int hi;
+    if constexpr (T == T_Q6_K) {
+        v = X.v[2 * e + (i & 1)];
+        hi = i >> 1;
+    } else if constexpr (T == T_NVFP4) {
+        v = X.v[i];
+        hi = e;
+    } else {
+        v = X.v[2 * e + (i >> 1)];
+        hi = i & 1;
+    }
+    return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+}
+
+// Half-group q of staged superblock cb, which is superblock cb0 + cb*stride of x.
+template <int T>
+__device__ __forceinline__ void xhalf_fetch(const MmaArgs &A, int q, int cb0, int stride, XHalf &X) {
+    const int n = A.n, h = q & 1, r = q >> 1;
+    const int t = n == 1 ? 0 : r % n, cg = n == 1 ? r : r / n, g = cg & 3, cb = cg >> 2;
+    const _Float16 *p = reinterpret_cast<const _Float16 *>(A.x) + (int64_t)t * A.k + (int64_t)(cb0 + cb * stride) * 256 +
+                        xhalf_base<T>(g, h);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(p + xhalf_off<T>(l));
+        X.v[l] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
+// Writes the half-group's four units (if `st`: the lane's half-group exists).
+template <int T>
+__device__ __forceinline__ void xhalf_commit(int q, bool st, const XHalf &X, uint4 *xs) {
+    uint4 *u = xs + (q >> 1) * kUnitsPerTok + 4 * (q & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint2 p0 = xhalf_piece<T>(X, i, 0), p1 = xhalf_piece<T>(X, i, 1);
+        uint4 v;
+        if constexpr (T == T_Q4_K || T == T_Q5_K) {
+            // [x0 x1 x2 x3] -> [x0 x2] [x1 x3]
+            v.x = __builtin_amdgcn_perm(p0.y, p0.x, 0x05040100u);
+            v.y = __builtin_amdgcn_perm(p0.y, p0.x, 0x07060302u);
+            v.z = __builtin_amdgcn_perm(p1.y, p1.x, 0x05040100u);
+            v.w = __builtin_amdgcn_perm(p1.y, p1.x, 0x07060302u);
+        } else {
+            v = make_uint4(p0.x, p0.y, p1.x, p1.y);
+        }
+        if (st) u[i] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q4_K / Q5_K weight operand of step s.  Quant dword s of the lane's chunk (bytes
+// 4s..4s+3 = positions 4s..4s+3 of sub-blocks 2g (low nibbles) and 2g+1 (high)):
+//   lo02 = 1024 + q at (4s, 4s+2), lo13 at (4s+1, 4s+3)     [fp16 magic, exact]
+//   hi02 = 256 + 4q at (32+4s, 34+4s), hi13 at (33+4s, 35+4s)
+// sc*q = (1024+q)*sc - 1024*sc = (256+4q)*(sc/4) - 64*sc with one fused rounding
+// of an exactly representable value.
+struct KqTile {
+    h2 S0, B0, S1, B1;
+    h8 bm;           // min operand: m_2g on the low-sub-block slots, m_2g+1 on the high ones
+    float d, dmin;
+};
+
+__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, int g) {
+    const KqLane L = kq_lane_consts(g);
+    const uint32_t t1 = __builtin_amdgcn_perm(R.hdr.w, R.hdr.y, L.sel);
+    const uint32_t t2 = __builtin_amdgcn_perm(R.hdr.w, R.hdr.z, L.sel);
+    const uint32_t sc = (t1 & L.mask) | ((t1 >> 18) & 0x3030u);
+    const uint32_t mn = ((t2 >> L.shm) & L.mask) | ((t2 >> 18) & 0x3030u);
+    const float sc0 = (float)(sc & 0xFFu), sc1 = (float)((sc >> 8) & 0xFFu);
+    KqTile k;
+    k.S0 = h2c(sc0);
+    k.B0 = h2c(-1024.0f * sc0);
+    k.S1 = h2c(0.25f * sc1);
+    k.B1 = h2c(-64.0f * sc1);
+    const uint32_t m0 = as_u32(h2c((float)(mn & 0xFFu))), m1 = as_u32(h2c((float)((mn >> 8) & 0xFFu)));
+    k.bm = mk_h8(m0, m0, m1, m1);
+    k.d = f16lo(R.hdr.x);
+    k.dmin = f16hi(R.hdr.x);
+    return k;
+}
+
+template <bool Q5>
+__device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, int s) {
+    const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+    const uint32_t w = qw[s], w8 = w >> 8;
+    uint32_t lo02 = and_or(w, 0x000F000Fu, 0x64006400u);
+    uint32_t lo13 = and_or(w8, 0x000F000Fu, 0x64006400u);
+    uint32_t hi02 = and_or(w, 0x00F000F0u, 0x5C005C00u);
+    uint32_t hi13 = and_or(w8, 0x00F000F0u, 0x5C005C00u);
+    if (Q5) {
+        // fifth bits: bit 2g (low sub-block) and 2g+1 (high) of qh byte l
+        const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
+        const uint32_t hs = hw[s] >> (2 * g);
+        lo02 = and_or(hs << 4, 0x00100010u, lo02);
+        lo13 = and_or(hs >> 4, 0x00100010u, lo13);
+        hi02 = and_or(hs << 7, 0x01000100u, hi02);
+        hi13 = and_or(hs >> 1, 0x01000100u, hi13);
+    }
+    return mk_h8(pk_fma(lo02, K.S0, K.B0), pk_fma(lo13, K.S0, K.B0), pk_fma(hi02, K.S1, K.B1),
+                 pk_fma(hi13, K.S1, K.B1));
+}
+
+// Q6_K.  Lane chunk g = half h6 = g >> 1, quarter q6 = g & 1 (positions 16*q6 ..
+// 16*q6+15 of each of the four 32-weight groups of the half).  Dword i of the
+// runs A (groups 0, 2), B (groups 1, 3) and H (high bits) covers positions 4i..4i+3;
+// q6_oct gives 1024 + q for groups 0, 1 and 256 + 4q for groups 2, 3 (byte-paired,
+// positions in natural order).  Step s = 2i + e takes groups 2e (pairs 0, 1) and
+// then 2e + 1, positions 4i .. 4i+3 of each.  The weight operand is
+//   (v - 1056) * sc   (groups 0, 1)      (v - 384) * (sc/4)   (groups 2, 3).
+struct Q6Tile {
+    h2 S[4];
+    float d;
+};
+
+// The aligned dword after each of the lane's runs A, B, H is the first dword of a
+// run another lane of the same row loaded (lane chunk g = 2s + h):
+//   after A_g: A_{g+1} (h = 0) or B_{g-1} (h = 1)                   lane ^ 16
+//   after B_g: B_{g+1} (g = 0, 2), A_2 (g = 1), H_0 (g = 3)         lane + 16
+//   after H_g: H_{g+1} (g = 0..2), scale bytes 0..3 (g = 3, from g = 0)   lane + 16
+// Each source lane publishes the one value its requester needs.
+__device__ __forceinline__ void q6_extras(MRawQ6 &R, int g) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int nxt = (lane + 16) & 63;
+    R.a4 = (uint32_t)__shfl((int)((g & 1) ? R.a.x : R.b.x), lane ^ 16);
+    R.b4 = (uint32_t)__shfl((int)(g == 0 ? R.h.x : (g == 2 ? R.a.x : R.b.x)), nxt);
+    R.h4 = (uint32_t)__shfl((int)(g == 0 ? R.s0 : R.h.x), nxt);
+}
+
+__device__ __forceinline__ Q6Tile q6_tile(const MRawQ6 &R, int g) {
+    const uint32_t l0 = __builtin_amdgcn_alignbyte(R.s1, R.s0, R.mis);
+    const uint32_t l1 = __builtin_amdgcn_alignbyte(R.s2, R.s1, R.mis);
+    const int sh = 8 * (g & 1);
+    // scale of group grp: sub-block 8*h6 + 2*grp + q6 (grp 0, 1 in l0; 2, 3 in l1)
+    Q6Tile k;
+    k.S[0] = h2c(i8_at(l0, sh));
+    k.S[1] = h2c(i8_at(l0, sh + 16));
+    k.S[2] = h2c(0.25f * i8_at(l1, sh));
+    k.S[3] = h2c(0.25f * i8_at(l1, sh + 16));
+    k.d = f16lo(R.d);
+    return k;
+}
+
+// Dword I (and I + 1, for re-alignment) of a 16-byte run followed by its extra dword.
+template <int I>
+__device__ __forceinline__ uint32_t run_pair(uint4 v, uint32_t extra, uint32_t sel) {
+    if constexpr (I == 0) return pair_bytes(v.y, v.x, sel);
+    else if constexpr (I == 1) return pair_bytes(v.z, v.y, sel);
+    else if constexpr (I == 2) return pair_bytes(v.w, v.z, sel);
+    else return pair_bytes(extra, v.w, sel);
+}
+
+// The two steps 2I, 2I+1 of dword I.
+template <int I>
+__device__ __forceinline__ void q6_steps(const MRawQ6 &R, const Q6Tile &K, h8 &b0, h8 &b1) {
+    const uint32_t sel = R.mis ? kSelMis : kSelAligned;
+    const Q6Oct o = q6_oct(run_pair<I>(R.a, R.a4, sel), run_pair<I>(R.b, R.b4, sel), run_pair<I>(R.h, R.h4, sel));
+    const h2 B01 = h2c(-1056.0f), B23 = h2c(-384.0f);
+    b0 = mk_h8(as_u32((as_h2(o.v[0][0]) + B01) * K.S[0]), as_u32((as_h2(o.v[0][1]) + B01) * K.S[0]),
+               as_u32((as_h2(o.v[1][0]) + B01) * K.S[1]), as_u32((as_h2(o.v[1][1]) + B01) * K.S[1]));
+    b1 = mk_h8(as_u32((as_h2(o.v[2][0]) + B23) * K.S[2]), as_u32((as_h2(o.v[2][1]) + B23) * K.S[2]),
+               as_u32((as_h2(o.v[3][0]) + B23) * K.S[3]), as_u32((as_h2(o.v[3][1]) + B23) * K.S[3]));
+}
+
+// NVFP4 step s: codes 8s .. 8s+7 of the lane's 64 (low nibble first), scale s >> 1.
+__device__ __forceinline__ h8 f4_step(const MRawF4 &R, int s) {
+    const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+    const h2 S = h2c(e4m3_at(R.sc, s >> 1));   // e4m3 values are exact in fp16
+    return mk_h8(pk_mul(fp4_pair(qw[s], 0), S), pk_mul(fp4_pair(qw[s], 1), S), pk_mul(fp4_pair(qw[s], 2), S),
+                 pk_mul(fp4_pair(qw[s], 3), S));
+}
+
+template <int I, int NG>
+__device__ __forceinline__ void q6_dword(const MRawQ6 &R, const Q6Tile &K, const uint4 *const (&xv)[NG], f4 (&c1)[NG]) {
+    h8 b0, b1;
+    q6_steps<I>(R, K, b0, b1);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        c1[q] = mfma(u4h8(xv[q][2 * I]), b0, c1[q]);
+        c1[q] = mfma(u4h8(xv[q][2 * I + 1]), b1, c1[q]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One superblock of NT weight tiles for NG token groups.  xa[q] = the lane's nine
+// units of the superblock for token group q (or the zeros), read up front.
+template <int T, int NT, int NG>
+__device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int g, const uint4 *const (&xa)[NG],
+                                    f4 (&acc)[NT][NG]) {
+    const uint4 *const(&xv)[NG] = xa;   // LDS reads at their use; other waves hide the latency
+    if constexpr (T == T_Q4_K || T == T_Q5_K) {
+        // c1 = sum_k sc*q*x and c2 = sum_k m*x over the superblock (m of the
+        // position's sub-block), both from the same x operands; y += d*c1 - dmin*c2.
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const KqTile K = kq_tile(R[i], g);
+            f4 c1[NG], c2[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) c1[q] = c2[q] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const h8 b = kq_step<T == T_Q5_K>(R[i], K, g, s);
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    const h8 a = u4h8(xv[q][s]);
+                    c1[q] = mfma(a, b, c1[q]);
+                    c2[q] = mfma(a, K.bm, c2[q]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = __builtin_fmaf(K.d, c1[q][e], acc[i][q][e]);
+                    acc[i][q][e] = __builtin_fmaf(-K.dmin, c2[q][e], v);
+                }
+        }
+    } else if constexpr (T == T_Q6_K) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            MRawQ6 Ri = R[i];
+            q6_extras(Ri, g);
+            const Q6Tile K = q6_tile(Ri, g);
+            f4 c1[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
+            q6_dword<0, NG>(Ri, K, xv, c1);
+            q6_dword<1, NG>(Ri, K, xv, c1);
+            q6_dword<2, NG>(Ri, K, xv, c1);
+            q6_dword<3, NG>(Ri, K, xv, c1);
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(K.d, c1[q][e], acc[i][q][e]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const h8 b = f4_step(R[i], s);
+#pragma unroll
+                for (int q = 0; q < NG; ++q) acc[i][q] = mfma(u4h8(xv[q][s]), b, acc[i][q]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Staging of x chunk [cb0, cb1) into LDS by the whole workgroup (8*n*cl
+// half-groups; blockDim is even, so the two halves of a group share a wave).
+template <int T>
+__device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, int cb1) {
+    const int halves = 8 * A.n * (cb1 - cb0);
+    const int w64 = 64 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    for (int q0 = 0; q0 < halves; q0 += (int)blockDim.x) {   // uniform trip count
+        if (q0 + w64 < halves) {                              // scalar: the wave has half-groups
+            const int q = q0 + (int)threadIdx.x;
+            XHalf X;
+            xhalf_fetch<T>(A, q < halves ? q : halves - 1, cb0, 1, X);
+            xhalf_commit<T>(q, q < halves, X, xu);
+        }
+    }
+}
+
+// The body for one weight type.  The wave serves NT row tiles (`wr[i]`/`sr[i]` = its
+// lane's row in tile i and the NVFP4 scales of that row) and its superblocks
+// b = kp + i*KS, i = 0 .. cnt-1, in increasing order (kp and KS are wave-uniform
+// scalars).
+//
+// Decode path: when every wave's superblocks fit one round of loads and their x
+// fits one staging half-group per lane, each wave stages its own x (see below).  Otherwise a ring of kDepth superblocks
+// refills behind the computation, and x is staged in chunks of A.kc superblocks in
+// turn; every wave steps through every chunk (two barriers per step), whether or
+// not it has superblocks there, so all waves meet the same barriers.
+template <int T, int NT, int NG>
+__device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool dec, int g, int t,
+                                         const uint8_t *const (&wr)[NT], const uint8_t *const (&sr)[NT], uint4 *lds,
+                                         f4 (&acc)[NT][NG]) {
+    typedef typename MRawOf<T>::type Raw;
+    constexpr int D = NT == 1 ? kDepth : 2;
+    const int n = A.n, nb = A.nb, kc = A.kc;
+    const uint4 *zero = lds;   // kZeroUnits units of zeros
+    uint4 *xu = lds + kZeroUnits;
+    const int cnt = kp < nb ? (nb - 1 - kp) / KS + 1 : 0;   // wave-uniform
+    const int maxcnt = (nb + KS - 1) / KS;                    // workgroup-uniform (the cnt of kp = 0)
+    const int lastb = cnt > 0 ? kp + (cnt - 1) * KS : nb - 1;
+    const int nchunks = (nb + kc - 1) / kc;
+    const int tid = (int)threadIdx.x;
+    (void)nchunks;
+    // Lanes of tokens >= n read zeros (workgroup staging) or, in the decode path,
+    // which meets no barrier after the zeros are written, the wave's own units:
+    // their rows of the product are never stored.
+    auto xa_of = [&](int cb, const uint4 *(&xa)[NG], const uint4 *other) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            const int tok = 16 * q + t;
+            xa[q] = tok < n ? xu + ((cb * 4 + g) * n + tok) * kUnitsPerTok : other;
+        }
+    };
+
+    if (dec) {   // the host guarantees maxcnt <= D and 8 * n * maxcnt <= 64 * kMmaDecRounds
+        // Each wave stages the x of its own superblocks in a region of its own: its x
+        // loads go out ahead of its weight loads, the in-order load counter lets it
+        // wait for x alone, and no barrier ties it to the other waves (whose loads,
+        // queued in the same memory pipeline, would otherwise set the pace).  Slot 0
+        // is issued with x; slot u + 1 goes out just before slot u is computed.
+        // Every slot is loaded unconditionally (a slot past the wave's last
+        // superblock re-reads superblock `lastb`, a cache hit, and is not used), so
+        // the loads outstanding at each wait are known at compile time.
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        xu += wave * (maxcnt * 4 * n * kUnitsPerTok);
+        const int hq = 8 * n * cnt;   // this wave's half-groups (wave-uniform), one per lane and round
+        Raw ring[D][NT];
+        if (hq <= 64) {   // scalar: one round, its loads ahead of the weight loads
+            XHalf X;
+            if (cnt > 0) xhalf_fetch<T>(A, lane < hq ? lane : hq - 1, kp, KS, X);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kp, lastb), g);
+            if (cnt > 0) xhalf_commit<T>(lane, lane < hq, X, xu);   // LDS order within a wave: no barrier
+        } else {          // several rounds (several tokens), all staged before the weight loads
+            for (int q0 = 0; q0 < hq; q0 += 64) {
+                XHalf X;
+                const int q = q0 + lane;
+                xhalf_fetch<T>(A, q < hq ? q : hq - 1, kp, KS, X);
+                xhalf_commit<T>(q, q < hq, X, xu);
+            }
+#pragma unroll
+            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kp, lastb), g);
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            if (u + 1 < D) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(kp + (u + 1) * KS, lastb), g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (u < cnt) {   // scalar branch
+                const uint4 *xa[NG];
+                xa_of(u, xa, xu);
+                msb<T, NT, NG>(ring[u], g, xa, acc);
+            }
+        }
+        return;
+    }
+
+    x_stage<T>(A, xu, 0, min(nb, kc));   // ahead of the weight loads, as above
+    Raw ring[D][NT];
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(kp + u * KS, lastb), g);
+    __syncthreads();
+    int chunk = 0;
+    for (int i0 = 0; i0 < cnt; i0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int it = i0 + u;
+            if (it < cnt) {   // scalar branch
+                const int b = kp + it * KS;
+                while (b >= (chunk + 1) * kc) {   // scalar
+                    ++chunk;
+                    __syncthreads();
+                    x_stage<T>(A, xu, chunk * kc, min(nb, (chunk + 1) * kc));
+                    __syncthreads();
+                }
+                const uint4 *xa[NG];
+                xa_of(b - chunk * kc, xa, zero);
+                msb<T, NT, NG>(ring[u], g, xa, acc);
+            }
+            if (i0 + D < cnt) {   // refill only when the ring has more to serve
+#pragma unroll
+                for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(kp + (it + D) * KS, lastb), g);
+            }
+        }
+    }
+    // Step through the remaining chunks so every wave meets the same barriers.
+    while (chunk + 1 < nchunks) {
+        ++chunk;
+        __syncthreads();
+        x_stage<T>(A, xu, chunk * kc, min(nb, (chunk + 1) * kc));
+        __syncthreads();
+    }
+}
+
+// WV waves per workgroup = WV / KS tile groups x KS superblock phases.  A wave
+// serves NT weight tiles of 16 rows that share the x operands:
+//   NT = 1: rows 16u .. 16u+15 of the matrix;
+//   NT = 2, S.data2 set (SW, or a same-shape pair): rows 16u .. 16u+15 of the
+//           matrix and of data2 (SW: gate and up; y gets silu(gate) * up);
+//   NT = 2, S.data2 null: rows 32u .. 32u+15 and 32u+16 .. 32u+31 of the matrix.
+// Which wave serves a row never changes the row's instructions.
+// Single-tile, single-group Q4_K / NVFP4 launches ask for five waves per SIMD (at
+// most 96 VGPRs), so that the 4864 waves of a gate/up pair at KS = 4 are all resident
+// at once; the others take what their ring of loads needs.
+template <int TS, int NG, int NT>
+constexpr int mma_min_waves() {
+    return ((TS & ~(TS_Q4 | TS_F4)) == 0 && NG == 1 && NT == 1) ? 5 : 1;
+}
+
+template <int TS, int NG, int WV, int NT, bool SW>
+__global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT>())) void mma_kernel(MmaArgs A) {
+    static_assert(NT == 1 || NT == 2, "one or two tiles per wave");
+    static_assert(!SW || NT == 2, "SwiGLU serves gate and up tiles");
+    extern __shared__ uint4 lds[];
+    const int bid = (int)blockIdx.x;
+    const bool in1 = A.nseg > 1 && bid >= A.seg[1].wg_begin;
+    const bool in2 = A.nseg > 2 && bid >= A.seg[2].wg_begin;
+    const MSeg S = in2 ? A.seg[2] : (in1 ? A.seg[1] : A.seg[0]);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // scalar
+    const int KS = S.ks, lks = __builtin_ctz((unsigned)KS), tpw = WV >> lks;
+    const int kp = wave & (KS - 1), rt = wave >> lks;
+    const int j = lane & 15, g = lane >> 4;
+    const bool two_mats = NT == 2 && (SW || S.data2 != nullptr);   // segment-uniform
+    const int64_t unit = (int64_t)(bid - S.wg_begin) * tpw + rt;
+    int64_t rows[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) rows[i] = (NT == 2 && !two_mats) ? unit * 32 + 16 * i + j : unit * 16 + j;
+    const int n = A.n;
+    if (threadIdx.x < kZeroUnits) lds[threadIdx.x] = make_uint4(0, 0, 0, 0);
+
+    const uint8_t *wr[NT];
+    const uint8_t *sr[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int64_t r = rows[i] < S.m ? rows[i] : S.m - 1;   // rows past m read row m-1; results dropped
+        const bool second = two_mats && i == 1;
+        wr[i] = (second ? S.data2 : S.data) + r * S.row_bytes;
+        sr[i] = S.type == T_NVFP4 ? (second ? S.scales2 : S.scales) + r * (S.row_bytes / 8) : nullptr;
+    }
+    f4 acc[NT][NG];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int q = 0; q < NG; ++q) acc[i][q] = (f4){0.f, 0.f, 0.f, 0.f};
+    if ((TS & TS_Q4) && S.type == T_Q4_K)
+        mma_body<T_Q4_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+    else if ((TS & TS_Q5) && S.type == T_Q5_K)
+        mma_body<T_Q5_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+    else if ((TS & TS_Q6) && S.type == T_Q6_K)
+        mma_body<T_Q6_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+    else if ((TS & TS_F4) && S.type == T_NVFP4)
+        mma_body<T_NVFP4, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+
+    // Partials of the KS waves of a row tile, added in wave order.
+    if (KS > 1) {
+        constexpr int per = NT * NG;   // 16-byte partials per lane
+        f4 *part = reinterpret_cast<f4 *>(lds);
+        __syncthreads();
+        if (kp != 0) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) part[(wave * per + i * NG + q) * 64 + lane] = acc[i][q];
+        }
+        __syncthreads();
+        if (kp != 0) return;
+        for (int w = 1; w < KS; ++w) {
+            const int src = wave + w;
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    const f4 p = part[(src * per + i * NG + q) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][q][e] += p[e];
+                }
+        }
+    }
+    if (SW) {
+        if (rows[0] < S.m) {
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 16 * q + 4 * g + e;
+                    if (tok < n) {
+                        const float gv = acc[0][q][e];
+                        S.y[(int64_t)tok * S.m + rows[0]] = gv / (1.0f + __expf(-gv)) * acc[NT - 1][q][e];
+                    }
+                }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const bool second = two_mats && i == 1;
+        float *y = second ? S.y2 : S.y;
+        const float *resid = second ? nullptr : S.resid;
+        if (rows[i] < S.m) {
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 16 * q + 4 * g + e;
+                    if (tok < n) {
+                        const int64_t o = (int64_t)tok * S.m + rows[i];
+                        float v = acc[i][q][e];
+                        if (resid) v = resid[o] + v;
+                        y[o] = v;
+                    }
+                }
+        }
+    }
+}
+
+}  // namespace qg

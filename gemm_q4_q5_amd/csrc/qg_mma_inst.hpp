@@ -1,0 +1,48 @@
+// Instantiations of the row-invariant MFMA product for one workgroup size
+// (included by qg_mma_w4.hip, qg_mma_w8.hip and qg_mma_w16.hip).
+#pragma once
+#include "qg_mma.hpp"
+
+namespace qg {
+
+template <int TS, int NG, int WV, int NT, bool SW>
+static hipError_t launch_one(const MmaArgs &A, int grid, size_t lds, hipStream_t st) {
+    const void *fn = (const void *)mma_kernel<TS, NG, WV, NT, SW>;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((mma_kernel<TS, NG, WV, NT, SW>), dim3(grid), dim3(64 * WV), lds, st, A);
+    return hipGetLastError();
+}
+
+template <int NG, int WV, int NT, bool SW>
+static hipError_t launch_ts(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
+    switch (ts) {
+    case TS_Q4: return launch_one<TS_Q4, NG, WV, NT, SW>(A, grid, lds, st);
+    case TS_Q5: return launch_one<TS_Q5, NG, WV, NT, SW>(A, grid, lds, st);
+    case TS_Q6: return launch_one<TS_Q6, NG, WV, NT, SW>(A, grid, lds, st);
+    case TS_F4: return launch_one<TS_F4, NG, WV, NT, SW>(A, grid, lds, st);
+    default:
+        if constexpr (SW) return hipErrorInvalidValue;   // SwiGLU pairs share one type
+        else if (ts == (TS_Q4 | TS_Q6)) return launch_one<TS_Q4 | TS_Q6, NG, WV, NT, false>(A, grid, lds, st);
+        else return launch_one<TS_ALL, NG, WV, NT, false>(A, grid, lds, st);
+    }
+}
+
+template <int NG, int WV>
+static hipError_t launch_nt(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
+    if (A.mode == MODE_SWIGLU) return launch_ts<NG, WV, 2, true>(A, ts, grid, lds, st);
+    if (A.nt == 2) {
+        if constexpr (WV <= 8) return launch_ts<NG, WV, 2, false>(A, ts, grid, lds, st);
+        else return hipErrorInvalidValue;
+    }
+    return launch_ts<NG, WV, 1, false>(A, ts, grid, lds, st);
+}
+
+template <int WV>
+static hipError_t launch_wv(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
+    return A.n > 16 ? launch_nt<2, WV>(A, ts, grid, lds, st) : launch_nt<1, WV>(A, ts, grid, lds, st);
+}
+
+}  // namespace qg

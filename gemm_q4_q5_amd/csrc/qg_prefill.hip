@@ -11,7 +11,7 @@
 // with fp32 accumulation.  The next step's global loads are issued before the
 // current step's MFMAs.  No row-invariance contract (TandemLLM Kernels page,
 // "Prefill kernels"): the result is deterministic, but not the decode kernel's bits.
-#include "qg_gemv.hpp"
+#include "qg_loads.hpp"
 #include "qg_prefill.h"
 
 namespace qg {
@@ -27,24 +27,20 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     return as_u32((h2){(_Float16)lo, (_Float16)hi});
 }
 
-// One dequant task = the 64 weights a GEMV lane of chunk c owns in one
-// superblock (the GEMV kernels' loads and unpacking are reused): step kt covers
+// One dequant task = the 64 weights of chunk c of one superblock (the probe's
+// loads and unpacking are reused): step kt covers
 // half s = kt & 1 of superblock kt >> 1, and its two tasks per weight row are
 // chunks c = 2s + hf (hf = 0, 1).
 template <int T>
-__device__ __forceinline__ typename Pol<T>::Raw p_load(const PrefillArgs &A, int64_t r, int kt, int hf) {
+__device__ __forceinline__ typename Loader<T>::Raw p_load(const PrefillArgs &A, int64_t r, int kt, int hf) {
     const int b = kt >> 1, c = 2 * (kt & 1) + hf;
-    Seg S;
-    S.data = A.data;
-    S.scales = A.scales;
-    S.row_bytes = A.row_bytes;
-    return Pol<T>::load(S, r, b, c);
+    return Loader<T>::load(A.data, A.scales, A.row_bytes, r, b, c);
 }
 
 // Write the task's 64 weights (fp16, one rounding of the exact fp32 value) into
 // the LDS row of the step, at their K offsets within the step.
 template <int T>
-__device__ __forceinline__ void p_store(const typename Pol<T>::Raw &R, int kt, int hf, _Float16 *wrow) {
+__device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt, int hf, _Float16 *wrow) {
     const int c = 2 * (kt & 1) + hf;
     if (T == T_Q4_K || T == T_Q5_K) {
         // chunk c: sub-block 2c at step offsets 64hf + 0..31, 2c+1 at 64hf + 32..63
@@ -149,7 +145,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
 
     const uint4 *xg = reinterpret_cast<const uint4 *>(A.x);
     uint4 xv[XV];
-    typename Pol<T>::Raw raw;
+    typename Loader<T>::Raw raw;
     auto fetch = [&](int kt) {
 #pragma unroll
         for (int v = 0; v < XV; ++v) {
