@@ -385,7 +385,8 @@ def main():
         ach = bytes1["pair"] / (pair_us * 1e3)
         res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                           "traffic": load_traffic(sha), "kernel": "gemv_kernel<1> (qgemv_pair)",
+                           "traffic": load_traffic(sha),
+                           "kernel": "qg::mma_kernel<1, 1, 4, 1, false> (qgemv_pair, Q4_K, one token)",
                            "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
     if not args.no_n32:
         r32 = time_layer(layers, 32, max(LAYERS, args.steps // 4), LAYERS)
