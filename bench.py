@@ -13,7 +13,10 @@ the 256 MB Infinity Cache) rotate so every step streams its weights cold.  The
 overhead is not part of the measurement.
 
 Headline: achieved HBM GB/s (algorithmic bytes / time) at N=1, the figure the
-decode-GEMV pages care about; the same layer at N=32 is reported beside it.
+decode-GEMV pages care about.  Beside it: a plain read of the same weight bytes
+(the read-stream probe, same rotation and call order), the same layer at N=32,
+the 512-token prefill GEMM in TFLOP/s, NVFP4 at 1/16/32 rows on 16384x8192 and
+the 151936x2560 head, and the CPU oracle on a bounded sample.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -178,6 +181,79 @@ def time_layer(layers, n, steps, warmup):
     return out
 
 
+def _layer_regions(L):
+    """The weight tensors each layer call streams, in the layer's call order."""
+    W = L.W
+    return (("triple", [W["wq"].data, W["wk"].data, W["wv"].data]), ("add", [W["wo"].data]),
+            ("pair", [W["gate"].data, W["up"].data]), ("down", [W["down"].data]))
+
+
+def time_read_ceiling(layers, reps):
+    """The read-stream probe (plain 16-byte loads, no arithmetic) over the same
+    weight bytes, in the same 36-layer rotation and call order as the layer: the
+    HBM read rate this memory system gives the step's byte pattern and launch
+    count, against which the products are also reported."""
+    import torch
+    import gemm_q4_q5_amd as qg
+    out = torch.zeros(qg._lib.READ_PROBE_WORDS, dtype=torch.int32, device="cuda")
+    for _, regs in _layer_regions(layers[0]):
+        qg.qg_stream_read(regs, out)
+    torch.cuda.synchronize()
+    res = {}
+    for only in (None,) + KERNELS:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(LAYERS):
+                for name, regs in _layer_regions(layers[i % len(layers)]):
+                    if only is None or name == only:
+                        qg.qg_stream_read(regs, out)
+        us = 1000.0 * _time_graph(g, reps, 1) / (reps * LAYERS)
+        nbytes = sum(t.numel() for name, regs in _layer_regions(layers[0]) for t in regs
+                     if only is None or name == only)
+        res["layer" if only is None else only] = {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e3), 1),
+                                                  "bytes": nbytes}
+        del g
+    return res
+
+
+NVFP4_SHAPES = (("nvfp4_16384x8192", 16384, 8192), ("nvfp4_151936x2560", 151936, 2560))
+
+
+def time_nvfp4(reps=4):
+    """NVFP4 W4A16 at 1, 16 and 32 rows on the two large shapes (a 16384x8192
+    projection and the 151936x2560 output head), each rotated over enough distinct
+    copies to exceed 1 GiB so every call streams cold; one graph per (shape, n)."""
+    import torch
+    import gemm_q4_q5_amd as qg
+    import synth
+    res = {}
+    for i, (name, m, k) in enumerate(NVFP4_SHAPES):
+        data, scales = synth.weights(synth.NVFP4, m, k, synth.rng_for(4, i))
+        base = qg.QWeight.from_host(synth.NVFP4, data, m, k, scales, device="cuda")
+        wbytes = data.nbytes + scales.nbytes
+        copies = max(2, -(-(1 << 30) // wbytes))
+        ws = [base] + [qg.QWeight(synth.NVFP4, base.data.clone(), m, k, base.scales.clone())
+                       for _ in range(copies - 1)]
+        res[name] = {"copies": copies}
+        for n in (1, 16, 32):
+            x = torch.from_numpy(synth.activations(n, k, synth.rng_for(4, i, n))).to("cuda")
+            y = torch.empty((n, m), dtype=torch.float32, device="cuda")
+            qg.qgemm_rows(ws[0], x, y)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for w in ws:
+                    qg.qgemm_rows(w, x, y)
+            us = 1000.0 * _time_graph(g, reps, 1) / (reps * copies)
+            b = call_bytes(synth.NVFP4, m, k, n)
+            res[name][f"n{n}"] = {"us": round(us, 2), "GB/s": round(b / (us * 1e3), 1),
+                                  "pct_of_peak": round(100 * b / (us * 1e3) / PEAK_HBM_GBS, 2)}
+            del g
+        del ws, base
+        torch.cuda.empty_cache()
+    return res
+
+
 PREFILL = (("q4k_9728x2560", 12, 9728, 2560), ("q6k_2560x9728", 14, 2560, 9728), ("q5k_4096x2560", 13, 4096, 2560))
 PREFILL_N = 512
 PREFILL_COPIES = 4
@@ -318,6 +394,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-n32", action="store_true", help="skip the N=32 pass")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-GEMM pass")
+    ap.add_argument("--no-nvfp4", action="store_true", help="skip the NVFP4 large-shape pass")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-stream ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel", choices=KERNELS, default=None,
                     help="profile mode: replay only this call over the 36-layer rotation")
@@ -388,6 +466,11 @@ def main():
                            "traffic": load_traffic(sha),
                            "kernel": "qg::mma_kernel<1, 1, 4, 1, false> (qgemv_pair, Q4_K, one token)",
                            "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
+    if not args.no_ceiling:
+        ceil = time_read_ceiling(layers, max(1, r1["graph_replays"] // 2))
+        res["read_ceiling"] = ceil
+        res["pct_of_read_ceiling"] = round(100.0 * value / ceil["layer"]["GB/s"] * ceil["layer"]["bytes"]
+                                           / step_bytes, 2)
     if not args.no_n32:
         r32 = time_layer(layers, 32, max(LAYERS, args.steps // 4), LAYERS)
         b32 = layer_call_bytes(32)
@@ -399,6 +482,8 @@ def main():
                                      for k, v in r32["kernel_us"].items()}
     if not args.no_prefill:
         res["prefill_n512"] = time_prefill()
+    if not args.no_nvfp4:
+        res["nvfp4_large"] = time_nvfp4()
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res))

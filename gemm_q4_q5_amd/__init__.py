@@ -5,8 +5,8 @@ of include/qgemm.h; this package is its ctypes binding.
 """
 from ._lib import (MAX_ROWS, NVFP4, Q4_K, Q5_K, Q6_K, QGError, QWeight, lib, qdequant, qgemm_prefill, qgemm_rows,
                    qgemv, qgemv_add, qgemv_nvfp4, qgemv_pair, qgemv_pair_swiglu, qgemv_q4k, qgemv_q5k,
-                   qgemv_q6k, qgemv_triple, row_bytes)
+                   qgemv_q6k, qgemv_triple, qg_stream_read, row_bytes)
 
 __all__ = ["MAX_ROWS", "NVFP4", "Q4_K", "Q5_K", "Q6_K", "QGError", "QWeight", "lib", "qdequant", "qgemm_prefill",
            "qgemm_rows", "qgemv", "qgemv_add", "qgemv_nvfp4", "qgemv_pair", "qgemv_pair_swiglu",
-           "qgemv_q4k", "qgemv_q5k", "qgemv_q6k", "qgemv_triple", "row_bytes"]
+           "qgemv_q4k", "qgemv_q5k", "qgemv_q6k", "qgemv_triple", "qg_stream_read", "row_bytes"]

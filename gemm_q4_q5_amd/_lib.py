@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             "qgemv_pair_swiglu": ([W, W, p, fp, i32, p], ctypes.c_int),
             "qgemm_prefill": ([W, p, fp, i64, p], ctypes.c_int),
             "qdequant": ([W, fp, p], ctypes.c_int),
+            "qg_stream_read": ([ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64), i32, p, p],
+                               ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -205,4 +207,21 @@ def qdequant(w: QWeight, out=None):
     out = _out((w.m, w.k), w.data, out)
     cw = w.c()
     _check(lib().qdequant(ctypes.byref(cw), _ptr(out), _stream()))
+    return out
+
+
+READ_PROBE_WORDS = 2048
+
+
+def qg_stream_read(regions, out):
+    """Read-stream probe: XOR every 32-bit word of the device tensors `regions`
+    (one to three, each 16-byte aligned, a multiple of 16 bytes) into the int32
+    device tensor `out` (READ_PROBE_WORDS elements, updated in place: the XOR of
+    its words changes by the XOR of all words read)."""
+    if out.numel() < READ_PROBE_WORDS:
+        raise ValueError(f"out needs {READ_PROBE_WORDS} int32 words")
+    n = len(regions)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in regions])
+    nbytes = (ctypes.c_int64 * max(n, 1))(*[t.numel() * t.element_size() for t in regions])
+    _check(lib().qg_stream_read(ptrs, nbytes, n, _ptr(out), _stream()))
     return out

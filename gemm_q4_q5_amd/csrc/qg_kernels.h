@@ -28,4 +28,18 @@ struct DequantArgs {
 
 hipError_t launch_dequant(const DequantArgs &a, hipStream_t st);
 
+constexpr int kReadMaxRegions = 3;
+constexpr int kReadSlots = 64;         // XOR accumulators of the read probe ...
+constexpr int kReadSlotStride = 32;    // ... one per 128-byte line: out is 2048 words
+
+struct ReadArgs {
+    const uint4 *p[kReadMaxRegions];
+    int64_t n16[kReadMaxRegions];   // 16-byte units per region
+    uint32_t *out;
+    int32_t nreg;
+    int32_t pad;
+};
+
+hipError_t launch_stream_read(const ReadArgs &a, hipStream_t st);
+
 }  // namespace qg

@@ -6,7 +6,7 @@
 // whose dequantized weight tile is shared by every wave of the block (E5).  Here
 // a workgroup of four waves owns a BM x BN tile of Y (tokens x weight rows) and
 // walks K in 128-wide steps: it stages X[BM][128] and the dequantized W[BN][128]
-// (fp16, rounded from the fp32-rounded exact weight: |error| <= 2^-11 |w|) in LDS,
+// (fp16: the exact weight rounded once, to nearest even; |error| <= 2^-11 |w|) in LDS,
 // then each wave runs v_mfma_f32_16x16x32_f16 over its (BM/2) x (BN/2) sub-tile
 // with fp32 accumulation.  The next step's global loads are issued before the
 // current step's MFMAs.  No row-invariance contract (TandemLLM Kernels page,
@@ -47,8 +47,11 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
         const RawKq &Q = reinterpret_cast<const RawKq &>(R);
         const KqCoef cf = kq_coef(Q.hdr, kq_lane_consts(c));
         // w = a*q + b with the exact products a = d*sc, b = -dmin*m: q is recovered
-        // exactly from the fp16 magic value (v - 1024, v - 256 = 4q), then one fma
-        // rounds the exact weight to fp32 (and the store rounds it once more to fp16).
+        // exactly from the fp16 magic value (v - 1024, v - 256 = 4q).  The fma and
+        // the fp16 conversion compile to one mixed-precision fma with an fp16 result
+        // (v_fma_mix{lo,hi}_f16), which rounds the exact a*q + b once, straight to
+        // fp16; an fp32 result rounded again to fp16 would differ where the fp32
+        // value lands on an fp16 tie.
         const uint32_t qw[8] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w};
         const uint32_t hw[8] = {Q.h0.x, Q.h0.y, Q.h0.z, Q.h0.w, Q.h1.x, Q.h1.y, Q.h1.z, Q.h1.w};
         const h2 m0 = {(_Float16)1024.0f, (_Float16)1024.0f}, m1 = {(_Float16)256.0f, (_Float16)256.0f};

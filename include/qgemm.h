@@ -170,7 +170,7 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
  * prefill GEMM with scales decoded once per (row, sub-block) and one dequantized
  * weight tile shared by all waves of a block): Y[n][m] = X[n][k] W^T for any
  * n >= 1 and every weight type.  Each workgroup dequantizes its weight tile once
- * into fp16 in LDS (one rounding of the exact fp32 weight, |error| <= 2^-11 |w|)
+ * into fp16 in LDS (the exact weight rounded once, to nearest even; |error| <= 2^-11 |w|)
  * and multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
  * y fp32 [n][m].  Deterministic; no row-invariance contract ([TK] "Prefill
  * kernels": chunk kernels share work across rows and are checked by agreement).
@@ -182,6 +182,19 @@ int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *
  * element (the device decoders the products use).  out fp32 [m][k].
  */
 int qdequant(const qg_weight *w, float *out, void *stream);
+
+/*
+ * Read-stream probe, a measuring stick and not part of any product: reads the
+ * nreg (1..3) device regions ptrs[i] of bytes[i] bytes each once, with 16-byte
+ * vector loads and no arithmetic on the data, and XORs every 32-bit word of them
+ * into out, a device array of 2048 uint32 (128-byte aligned, updated in place and
+ * not cleared): the XOR of all 2048 words changes by the XOR of all words read.
+ * Timing it over the bytes a weight product streams gives the plain HBM read rate
+ * the product is compared with.  ptrs and bytes are host arrays; every region is
+ * 16-byte aligned and bytes[i] is a positive multiple of 16.  Errors: QG_ERR_NULL,
+ * QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_LAUNCH; nothing is launched on error.
+ */
+int qg_stream_read(const void *const *ptrs, const int64_t *bytes, int32_t nreg, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

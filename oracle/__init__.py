@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_row_bytes.argtypes, L.oracle_row_bytes.restype = [i32, i64], i64
         L.oracle_dequant.argtypes = [i32, p, p, i64, i64, i64, i64, p]
         L.oracle_dequant.restype = ctypes.c_int
+        L.oracle_dequant64.argtypes = [i32, p, p, i64, i64, i64, i64, p]
+        L.oracle_dequant64.restype = ctypes.c_int
         L.oracle_gemm.argtypes = [i32, p, p, i64, i64, p, i64, p, i64, p, p, i32]
         L.oracle_gemm.restype = ctypes.c_int
         L.oracle_last_threads.argtypes, L.oracle_last_threads.restype = [], i32
@@ -82,6 +84,19 @@ def dequant(wtype: int, data: np.ndarray, scales, m: int, k: int, r0: int = 0, n
     rc = lib().oracle_dequant(wtype, _ptr(data), _ptr(scales), m, k, r0, nr, _ptr(out))
     if rc:
         raise ValueError("oracle_dequant: bad arguments")
+    return out
+
+
+def dequant64(wtype: int, data: np.ndarray, scales, m: int, k: int, r0: int = 0, nr=None) -> np.ndarray:
+    """fp64 [nr, k]: the exact weights of rows r0 .. r0+nr-1 (dequant() rounds these
+    once to fp32)."""
+    nr = m - r0 if nr is None else nr
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    scales = None if scales is None else np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((nr, k), dtype=np.float64)
+    rc = lib().oracle_dequant64(wtype, _ptr(data), _ptr(scales), m, k, r0, nr, _ptr(out))
+    if rc:
+        raise ValueError("oracle_dequant64: bad arguments")
     return out
 
 

@@ -102,8 +102,10 @@ static void scale_min_6bit(const uint8_t *s, int j, int *sc, int *mn) {
     }
 }
 
-/* One Q4_K (has_high = 0) or Q5_K (has_high = 1) superblock -> 256 fp32 weights. */
-static void dequant_q45(const uint8_t *b, int has_high, float *w) {
+/* One Q4_K (has_high = 0) or Q5_K (has_high = 1) superblock -> its 256 weights,
+ * exact (d*sc*q and dmin*mn each have at most 22 significant bits, so their
+ * difference is exact in fp64). */
+static void dequant_q45(const uint8_t *b, int has_high, double *w) {
     double d = u16_at(b), dmin = u16_at(b + 2);
     const uint8_t *s = b + 4;
     const uint8_t *qh = b + 16;
@@ -117,13 +119,12 @@ static void dequant_q45(const uint8_t *b, int has_high, float *w) {
         if (has_high) q += 16 * ((qh[l] >> j) & 1);
         int sc, mn;
         scale_min_6bit(s, j, &sc, &mn);
-        /* d*sc*q and dmin*mn are exact in fp64; one rounding to fp32. */
-        w[p] = (float)(d * sc * q - dmin * mn);
+        w[p] = d * sc * q - dmin * mn;
     }
 }
 
-/* One Q6_K superblock -> 256 fp32 weights: value d * sc * (q - 32), q 6-bit. */
-static void dequant_q6(const uint8_t *b, float *w) {
+/* One Q6_K superblock -> its 256 weights d * sc * (q - 32), q 6-bit (exact). */
+static void dequant_q6(const uint8_t *b, double *w) {
     const uint8_t *ql = b, *qh = b + 128;
     const int8_t *sc = (const int8_t *)(b + 192);
     double d = u16_at(b + 208);
@@ -135,20 +136,21 @@ static void dequant_q6(const uint8_t *b, float *w) {
         int hi = (qh[32 * s + l] >> (2 * g)) & 3;
         int q = lo | (hi << 4);
         int si = 8 * s + 2 * g + l / 16;
-        w[p] = (float)(d * sc[si] * (q - 32));
+        w[p] = d * sc[si] * (q - 32);
     }
 }
 
 /* One NVFP4 row: element k is the low nibble of byte k/2 when k is even. */
-static void dequant_nvfp4_row(const uint8_t *codes, const uint8_t *scales, int64_t k, float *w) {
+static void dequant_nvfp4_row(const uint8_t *codes, const uint8_t *scales, int64_t k, double *w) {
     for (int64_t i = 0; i < k; i++) {
         uint8_t code = (codes[i / 2] >> (4 * (i % 2))) & 15;
-        w[i] = (float)(oracle_e2m1(code) * oracle_e4m3(scales[i / 16]));
+        w[i] = oracle_e2m1(code) * oracle_e4m3(scales[i / 16]);
     }
 }
 
+/* Row r, exact, in fp64. */
 static void dequant_row(int32_t type, const uint8_t *data, const uint8_t *scales,
-                        int64_t k, int64_t r, float *w) {
+                        int64_t k, int64_t r, double *w) {
     int64_t rb = oracle_row_bytes(type, k);
     const uint8_t *row = data + r * rb;
     switch (type) {
@@ -173,8 +175,23 @@ static int check_args(int32_t type, const uint8_t *data, const uint8_t *scales, 
     return 0;
 }
 
+/* The fp32 weight is the exact value rounded once (the C conversion rounds to
+ * nearest, ties to even). */
 int oracle_dequant(int32_t type, const uint8_t *data, const uint8_t *scales,
                    int64_t m, int64_t k, int64_t r0, int64_t nr, float *out) {
+    if (check_args(type, data, scales, m, k) || !out || r0 < 0 || nr < 0 || r0 + nr > m) return -1;
+    double *w = (double *)malloc(sizeof(double) * k);
+    if (!w) return -1;
+    for (int64_t i = 0; i < nr; i++) {
+        dequant_row(type, data, scales, k, r0 + i, w);
+        for (int64_t j = 0; j < k; j++) out[i * k + j] = (float)w[j];
+    }
+    free(w);
+    return 0;
+}
+
+int oracle_dequant64(int32_t type, const uint8_t *data, const uint8_t *scales,
+                     int64_t m, int64_t k, int64_t r0, int64_t nr, double *out) {
     if (check_args(type, data, scales, m, k) || !out || r0 < 0 || nr < 0 || r0 + nr > m) return -1;
     for (int64_t i = 0; i < nr; i++) dequant_row(type, data, scales, k, r0 + i, out + i * k);
     return 0;
@@ -204,7 +221,7 @@ int oracle_gemm(int32_t type, const uint8_t *data, const uint8_t *scales,
 #endif
 #pragma omp parallel
     {
-        float *w = (float *)malloc(sizeof(float) * k);
+        double *w = (double *)malloc(sizeof(double) * k);
         if (!w) {
 #pragma omp atomic write
             err = 1;
@@ -213,12 +230,13 @@ int oracle_gemm(int32_t type, const uint8_t *data, const uint8_t *scales,
             for (int64_t i = 0; i < nrows; i++) {
                 int64_t r = rows ? rows[i] : i;
                 dequant_row(type, data, scales, k, r, w);
+                for (int64_t kk = 0; kk < k; kk++) w[kk] = (float)w[kk];   /* the fp32 weight */
                 for (int64_t t = 0; t < n; t++) {
                     const double *xt = xd + t * k;
                     double acc = 0.0, acc_abs = 0.0;
                     for (int64_t kk = 0; kk < k; kk++) {
-                        acc += (double)w[kk] * xt[kk];
-                        acc_abs += fabs((double)w[kk]) * fabs(xt[kk]);
+                        acc += w[kk] * xt[kk];
+                        acc_abs += fabs(w[kk]) * fabs(xt[kk]);
                     }
                     y[t * nrows + i] = acc;
                     a[t * nrows + i] = acc_abs;

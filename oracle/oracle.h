@@ -28,9 +28,15 @@ double oracle_e2m1(uint8_t code);
 /* Bytes of one stored row (NVFP4: codes only). -1 if the type or k is invalid. */
 int64_t oracle_row_bytes(int32_t type, int64_t k);
 
-/* Dequantize rows [r0, r0+nr) of an m x k weight to fp32, out is [nr][k]. */
+/* Dequantize rows [r0, r0+nr) of an m x k weight to fp32 (the exact value rounded
+ * once, to nearest even), out is [nr][k]. */
 int oracle_dequant(int32_t type, const uint8_t *data, const uint8_t *scales,
                    int64_t m, int64_t k, int64_t r0, int64_t nr, float *out);
+
+/* The same rows as exact values in fp64 (every weight of the four formats is
+ * exactly representable there). */
+int oracle_dequant64(int32_t type, const uint8_t *data, const uint8_t *scales,
+                     int64_t m, int64_t k, int64_t r0, int64_t nr, double *out);
 
 /*
  * y[t][i] = sum_k w[rows[i]][k] * x[t][k]  (fp64, sequential k),

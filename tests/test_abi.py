@@ -110,3 +110,25 @@ def test_fused_validation():
     e, _e = w(type_=14)
     assert L.qgemv_pair_swiglu(a, e, FAKE, FAKE, 1, None) == -4
     assert L.qdequant(a, None, None) == -1
+
+
+def _regions(ptrs, sizes):
+    n = len(ptrs)
+    return (ctypes.c_void_p * max(n, 1))(*ptrs), (ctypes.c_int64 * max(n, 1))(*sizes)
+
+
+@pytest.mark.parametrize("ptrs,sizes,nreg,out,code", [
+    ([FAKE], [64], 0, FAKE, -2),            # no region
+    ([FAKE] * 4, [64] * 4, 4, FAKE, -2),    # more than three
+    ([FAKE], [40], 1, FAKE, -2),            # not a multiple of 16 bytes
+    ([FAKE], [0], 1, FAKE, -2),
+    ([FAKE + 8], [64], 1, FAKE, -5),        # misaligned region
+    ([FAKE], [64], 1, FAKE + 64, -5),       # out not 128-byte aligned
+    ([0], [64], 1, FAKE, -1),
+    ([FAKE], [64], 1, 0, -1),
+])
+def test_stream_read_validation(ptrs, sizes, nreg, out, code):
+    L = qg.lib()
+    p, b = _regions(ptrs, sizes)
+    assert L.qg_stream_read(p, b, nreg, out, None) == code
+    assert L.qg_last_error() != b""

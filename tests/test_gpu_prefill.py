@@ -1,9 +1,11 @@
 """GPU parity of the MFMA prefill GEMM against the CPU oracle.
 
-The weight tile is rounded once to fp16 before the matrix cores see it, so the
-output is held to |y - y_ref| <= 2e-3 * sum|w||x| against the oracle's exact fp64
-product, and -- much tighter -- to fp32-accumulation error against the fp64
-product of the fp16-rounded oracle weights (which pins the MFMA operand layout).
+The weight operand is the exact weight rounded once to fp16 (round to nearest
+even), so the output is held to |y - y_ref| <= 2e-3 * sum|w||x| against the
+oracle's fp64 product, and -- much tighter -- to fp32-accumulation error against
+the fp64 product of the oracle's exact weights rounded to fp16 (which pins the
+MFMA operand layout).  An identity input returns the operand itself, compared
+bit for bit.
 """
 import numpy as np
 import pytest
@@ -19,7 +21,10 @@ TYPES = [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4]
 
 
 @pytest.mark.parametrize("wt", TYPES)
-@pytest.mark.parametrize("m,k,n", [(300, 1024, 130), (64, 256, 1), (130, 768, 17), (1000, 512, 256)])
+# The last two shapes are large enough for the 128x128 and 128x64 tiles (at least
+# 256 workgroups), ragged in both dimensions; the others take the 64x64 tile.
+@pytest.mark.parametrize("m,k,n", [(300, 1024, 130), (64, 256, 1), (130, 768, 17), (1000, 512, 256),
+                                   (2000, 256, 2050), (1000, 512, 2000)])
 def test_prefill_vs_oracle(wt, m, k, n):
     import torch
     print(f"prefill type={wt} m={m} k={k} n={n}", flush=True)
@@ -31,7 +36,7 @@ def test_prefill_vs_oracle(wt, m, k, n):
     y_ref, a = oracle.gemm(wt, data, scales, m, k, x)
     assert_within(got, y_ref, a, what=f"prefill type {wt}")
     # fp64 product of the fp16-rounded weights: only fp32 accumulation error remains
-    w16 = oracle.dequant(wt, data, scales, m, k).astype(np.float16).astype(np.float64)
+    w16 = oracle.dequant64(wt, data, scales, m, k).astype(np.float16).astype(np.float64)
     y16 = x.astype(np.float64) @ w16.T
     a16 = np.abs(x.astype(np.float64)) @ np.abs(w16).T
     assert_within(got, y16, a16, tol=2e-6, what=f"prefill type {wt} vs fp16 weights")
@@ -45,3 +50,21 @@ def test_prefill_deterministic():
     b = bits(qg.qgemm_prefill(w, x))
     torch.cuda.synchronize()
     assert np.array_equal(a, b)
+
+
+# (m, k) with k tokens of an identity input: 64x64, 128x64 and 128x128 tiles.
+@pytest.mark.parametrize("wt", TYPES)
+@pytest.mark.parametrize("m,k", [(300, 512), (2000, 1280), (2048, 2048)])
+def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
+    """x = I (k tokens): y[t][r] is the kernel's fp16 operand for w[r][t] (one
+    nonzero product, exact in fp32), which must equal the oracle's exact weight
+    rounded once to fp16 -- not the fp32 weight rounded again, which differs where
+    the fp32 value lands on an fp16 tie."""
+    import torch
+    print(f"prefill operand type={wt} m={m} k={k}", flush=True)
+    w, data, scales = weight(wt, m, k, 231)
+    y = qg.qgemm_prefill(w, x_dev(np.eye(k, dtype=np.float16)))
+    torch.cuda.synchronize()
+    want = oracle.dequant64(wt, data, scales, m, k).astype(np.float16).astype(np.float32)
+    want = want + np.float32(0.0)   # the sum with the zero products turns -0 into +0
+    assert np.array_equal(bits(y.T.contiguous()), bits(torch.from_numpy(want)))

@@ -176,3 +176,39 @@ def test_generator_is_deterministic_and_in_range():
     import torch
     sv = torch.from_numpy(s).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     assert sv.min() >= 0.0097 and sv.max() <= 1.0
+
+
+@pytest.mark.parametrize("wtype", [12, 13, 14, 1001])
+def test_dequant64_rounds_once_to_dequant(orc, wtype):
+    """The fp32 weight is the exact weight rounded once (numpy's fp64 -> fp32
+    conversion rounds to nearest even)."""
+    m, k = 64, 512
+    data, scales = synth.weights(wtype, m, k, synth.rng_for(77, wtype))
+    exact = orc.dequant64(wtype, data, scales, m, k)
+    assert np.array_equal(exact.astype(np.float32), orc.dequant(wtype, data, scales, m, k))
+    assert np.array_equal(orc.dequant64(wtype, data, scales, m, k, r0=5, nr=3), exact[5:8])
+
+
+def test_dequant64_keeps_bits_fp32_drops():
+    """A Q4_K sub-block whose weights need more than 24 significant bits: d*sc*q
+    and dmin*m are computed here with exact rationals from the stored fields."""
+    import struct
+    from fractions import Fraction
+    orc_ = __import__("oracle")
+    d16, dmin16 = np.float16(2.0e-2), np.float16(7.0e-5)   # exponents 2^-6 and 2^-14 apart
+    sc, mn = 63, 61                                          # sub-block 0: s[0] = sc, s[4] = m
+    blk = bytearray(144)
+    blk[0:2] = struct.pack("<e", d16)
+    blk[2:4] = struct.pack("<e", dmin16)
+    blk[4 + 0] = sc
+    blk[4 + 4] = mn
+    for l in range(32):
+        blk[16 + l] = l % 16   # low nibble: q of position l in sub-block 0
+    w64 = orc_.dequant64(12, np.frombuffer(bytes(blk), np.uint8), None, 1, 256)[0]
+    w32 = orc_.dequant(12, np.frombuffer(bytes(blk), np.uint8), None, 1, 256)[0]
+    lost = 0
+    for l in range(32):
+        want = Fraction(float(d16)) * sc * (l % 16) - Fraction(float(dmin16)) * mn
+        assert Fraction(float(w64[l])) == want, l
+        lost += Fraction(float(w32[l])) != want
+    assert lost > 0   # the fp32 weights are rounded, the fp64 ones are not

@@ -41,7 +41,9 @@ MUTANTS = {
     "e4m3_subnormal": ("ldexp(f / 8.0, -6)", "ldexp(f / 8.0, -7)"),
     "e2m1_bias": ("ldexp(1.0 + 0.5 * f, e - 1)", "ldexp(1.0 + 0.5 * f, e)"),
     "fp16_subnormal_flush": ("v = ldexp((double)f, -24);", "v = 0.0;"),
-    "gemm_reversed_x": ("acc += (double)w[kk] * xt[kk];", "acc += (double)w[kk] * xt[k - 1 - kk];"),
+    "gemm_reversed_x": ("acc += w[kk] * xt[kk];", "acc += w[kk] * xt[k - 1 - kk];"),
+    "gemm_unrounded_weights": ("for (int64_t kk = 0; kk < k; kk++) w[kk] = (float)w[kk];", ""),
+    "q45_terms_in_fp32": ("w[p] = d * sc * q - dmin * mn;", "w[p] = (float)(d * sc * q) - (float)(dmin * mn);"),
     "gemm_transposed_out": ("y[t * nrows + i] = acc;", "y[i * n + t] = acc;"),
 }
 
@@ -51,11 +53,40 @@ def _load(path):
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.oracle_dequant.argtypes = [i32, p, p, i64, i64, i64, i64, p]
     L.oracle_gemm.argtypes = [i32, p, p, i64, i64, p, i64, p, i64, p, p, i32]
+    L.oracle_dequant64.argtypes = [i32, p, p, i64, i64, i64, i64, p]
     return L
 
 
+def _exact_block_ok(L):
+    """The exact-weight pin of test_oracle (rationals from the stored fields)."""
+    import struct
+    from fractions import Fraction
+    d16, dmin16 = np.float16(2.0e-2), np.float16(7.0e-5)
+    blk = bytearray(144)
+    blk[0:2] = struct.pack("<e", d16)
+    blk[2:4] = struct.pack("<e", dmin16)
+    blk[4], blk[8] = 63, 61
+    for l in range(32):
+        blk[16 + l] = l % 16
+    data = np.frombuffer(bytes(blk), np.uint8).copy()
+    out = np.empty(256, np.float64)
+    L.oracle_dequant64(12, data.ctypes.data, None, 1, 256, 0, 1, out.ctypes.data)
+    if not all(Fraction(float(out[l])) == Fraction(float(d16)) * 63 * (l % 16) - Fraction(float(dmin16)) * 61
+               for l in range(32)):
+        return False
+    # one-hot x through the GEMM returns the fp32 weights exactly
+    x = np.eye(256, dtype=np.float16)
+    y = np.empty((256, 1)); a = np.empty((256, 1))
+    L.oracle_gemm(12, data.ctypes.data, None, 1, 256, x.view(np.uint16).ctypes.data, 256, None, 1,
+                  y.ctypes.data, a.ctypes.data, 1)
+    return np.array_equal(y[:, 0], out.astype(np.float32).astype(np.float64))
+
+
 def _pins_pass(L):
-    """True when every golden block and a numpy matmul check agree with library L."""
+    """True when every golden block, the exact-weight block and a numpy matmul
+    check agree with library L."""
+    if not _exact_block_ok(L):
+        return False
     for fx in json.load(open(GOLDEN))["fixtures"]:
         data = np.frombuffer(bytes.fromhex(fx["data"]), np.uint8).copy()
         sc = np.frombuffer(bytes.fromhex(fx["scales"]), np.uint8).copy() if "scales" in fx else None
