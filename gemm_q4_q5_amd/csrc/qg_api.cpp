@@ -124,15 +124,52 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     a.mode = mode;
     a.nt = fuse2 ? 2 : 1;
     // Workgroups of at least four waves; KS waves per row tile.
-    int wv = 4;
+    int wv0 = 4;
     int ks[3] = {1, 1, 1};
     for (int s = 0; s < a.nseg; ++s) {
         ks[s] = choose_ks(w[s]->type, w[s]->m, k);
-        wv = std::max(wv, ks[s]);
+        wv0 = std::max(wv0, ks[s]);
     }
-    if (!sw && a.nt == 2 && wv > 8) {   // a plain pair takes two tiles per wave only up to 8 waves
+    if (!sw && a.nt == 2 && wv0 > 8) {   // a plain pair takes two tiles per wave only up to 8 waves
         a.nt = 1;
         a.nseg = 2;
+    }
+    const int ng = n > 16 ? 2 : 1;
+    const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
+    // Decode path (each wave stages its own x) where a wave's superblocks fit one
+    // round of loads and their x one staging half-group per lane.
+    const int depth = a.nt == 2 ? 2 : qg::kMmaDepth;
+    auto dec_ok = [&](int s, int wv) {
+        const int maxcnt = (a.nb + ks[s] - 1) / ks[s];
+        const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
+        return maxcnt <= depth && 8 * n * maxcnt <= 64 * qg::kMmaDecRounds && need <= kMmaLdsBudget;
+    };
+    auto grid_of = [&](int wv) {
+        int gr = 0;
+        for (int s = 0; s < a.nseg; ++s) {
+            const int64_t rows_per_wg = 16 * (wv / ks[s]);
+            gr += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
+        }
+        return gr;
+    };
+    bool any_dec = false;
+    for (int s = 0; s < a.nseg; ++s) any_dec = any_dec || dec_ok(s, wv0);
+    // The general path stages x per workgroup in chunks of kc superblocks, and each
+    // chunk change costs a round of x loads behind the weight stream.  A grid of about
+    // one workgroup per CU (256 CUs) may take all of the CU's LDS for fewer, larger
+    // chunks, so the general path doubles the workgroup (more row tiles share each
+    // chunk) when that brings the grid down to that size.  At 32 tokens: down 35 -> 27
+    // us and Wo 16 -> 12 (already 160 workgroups), the triple 15 -> 12 and the gate/up
+    // pair 30 -> 27 (eight waves); larger grids keep 64 KB and two workgroups per CU.
+    constexpr int kOneRound = 320;
+    int wv = wv0;
+    if (!any_dec) {
+        const int wv_max = a.nt == 2 ? 8 : 16;
+        for (int cand = wv0; cand <= wv_max; cand *= 2)
+            if (grid_of(cand) <= kOneRound) {
+                wv = cand;
+                break;
+            }
     }
     a.wv = wv;
     int grid = 0;
@@ -155,26 +192,16 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         const int64_t rows_per_wg = 16 * (wv / ks[s]);
         grid += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
     }
-    const int ng = n > 16 ? 2 : 1;
-    const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
-    // The general path stages x in chunks of kc superblocks, and each chunk change costs
-    // a round of x loads behind the weight stream.  A grid that leaves at most one
-    // workgroup per CU (256 CUs) may take all of the CU's LDS for fewer, larger chunks
-    // (at 32 tokens: the 2560-row down and Wo calls, 27 vs 35 us and 11 vs 16 us);
-    // larger grids keep two workgroups per CU.
-    const size_t budget = grid <= 256 ? kMmaLdsMax : kMmaLdsBudget;
+    const size_t budget = grid <= kOneRound ? kMmaLdsMax : kMmaLdsBudget;
     const int kc = (int)std::max<size_t>(1, (budget - kMmaZeroBytes) / per_sb);
     a.kc = std::min(kc, a.nb);
-    size_t lds = kMmaZeroBytes + per_sb * a.kc;
-    // Decode path (each wave stages its own x) where a wave's superblocks fit one
-    // round of loads and their x one staging half-group per lane.
-    const int depth = a.nt == 2 ? 2 : qg::kMmaDepth;
+    size_t lds = kMmaZeroBytes;
     for (int s = 0; s < a.nseg; ++s) {
-        const int maxcnt = (a.nb + ks[s] - 1) / ks[s];
-        const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
-        if (maxcnt <= depth && 8 * n * maxcnt <= 64 * qg::kMmaDecRounds && need <= kMmaLdsBudget) {
+        if (dec_ok(s, wv)) {
             a.seg[s].dec = 1;
-            lds = std::max(lds, need);
+            lds = std::max(lds, kMmaZeroBytes + (size_t)wv * ((a.nb + ks[s] - 1) / ks[s]) * per_sb);
+        } else {   // the general path's x chunk
+            lds = std::max(lds, kMmaZeroBytes + per_sb * a.kc);
         }
     }
     const size_t part = (size_t)wv * 64 * 4 * (4 * ng * a.nt);   // partial sums of the K split
