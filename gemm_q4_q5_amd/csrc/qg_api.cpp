@@ -161,11 +161,14 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     // chunk) when that brings the grid down to that size.  At 32 tokens: down 35 -> 27
     // us and Wo 16 -> 12 (already 160 workgroups), the triple 15 -> 12 and the gate/up
     // pair 30 -> 27 (eight waves); larger grids keep 64 KB and two workgroups per CU.
+    // The general path takes at least eight waves (two row tiles per chunk of x at
+    // KS = 4): the 151936-row NVFP4 head at 16 / 32 tokens, 147 -> 95 / 207 -> 127 us.
     constexpr int kOneRound = 320;
     int wv = wv0;
     if (!any_dec) {
         const int wv_max = a.nt == 2 ? 8 : 16;
-        for (int cand = wv0; cand <= wv_max; cand *= 2)
+        wv = std::max(wv0, 8);
+        for (int cand = wv; cand <= wv_max; cand *= 2)
             if (grid_of(cand) <= kOneRound) {
                 wv = cand;
                 break;
