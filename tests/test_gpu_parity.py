@@ -174,12 +174,16 @@ def test_repeat_calls_are_bit_identical():
     assert np.array_equal(a, b)
 
 
-def test_swiglu_pair():
+# 3 tokens: the decode path; 20 and 32: the general path (gate and up tiles in one
+# wave, x staged per workgroup in 160 KB chunks).
+@pytest.mark.parametrize("m,n", [(384, 3), (384, 20), (3000, 32)])
+def test_swiglu_pair(m, n):
     import torch
-    m, k = 384, 2560
+    k = 2560
+    print(f"swiglu m={m} n={n}", flush=True)
     wg, dg, _ = weight(qg.Q4_K, m, k, 91)
     wu, du, _ = weight(qg.Q4_K, m, k, 92)
-    x = synth.activations(3, k, synth.rng_for(93))
+    x = synth.activations(n, k, synth.rng_for(93, n))
     h = qg.qgemv_pair_swiglu(wg, wu, x_dev(x))
     g, u = qg.qgemv_pair(wg, wu, x_dev(x))
     torch.cuda.synchronize()
