@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-Q4_K, Q5_K, Q6_K, NVFP4 = 12, 13, 14, 1001
+Q4_K, Q5_K, Q6_K, NVFP4, FP8 = 12, 13, 14, 1001, 1002
 
 
 def build(force: bool = True) -> str:
@@ -42,6 +42,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_fp16.argtypes, L.oracle_fp16.restype = [ctypes.c_uint16], ctypes.c_double
         L.oracle_e4m3.argtypes, L.oracle_e4m3.restype = [ctypes.c_uint8], ctypes.c_double
         L.oracle_e2m1.argtypes, L.oracle_e2m1.restype = [ctypes.c_uint8], ctypes.c_double
+        L.oracle_bf16.argtypes, L.oracle_bf16.restype = [ctypes.c_uint16], ctypes.c_double
         L.oracle_row_bytes.argtypes, L.oracle_row_bytes.restype = [i32, i64], i64
         L.oracle_dequant.argtypes = [i32, p, p, i64, i64, i64, i64, p]
         L.oracle_dequant.restype = ctypes.c_int
@@ -69,6 +70,10 @@ def e4m3(bits: int) -> float:
 
 def e2m1(code: int) -> float:
     return lib().oracle_e2m1(code)
+
+
+def bf16(bits: int) -> float:
+    return lib().oracle_bf16(bits)
 
 
 def row_bytes(wtype: int, k: int) -> int:

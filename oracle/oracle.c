@@ -20,6 +20,10 @@
  *    section; Performance page, Path C (#29).
  *  - NVFP4: 4-bit e2m1 weights with one e4m3 scale per 16 weights, product exact
  *    in fp16: TandemLLM Kernels page, "NVFP4 matrix products".
+ *  - Block-scaled FP8: e4m3 codes with one bf16 scale per 128 x 128 block, read as
+ *    stored: TandemLLM Kernels page, "FP8 matrix products".  Codes are [M][K];
+ *    the scale layout ([ceil(M/128)][K/128], row-major) is not printed there and is
+ *    this file's reading.
  *  Byte layouts inside a superblock are not printed on the pages; this file takes
  *  the public GGML K-quant layout (the plainest reading of "GGML K-quant").
  */
@@ -32,7 +36,7 @@
 #include <omp.h>
 #endif
 
-enum { T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_NVFP4 = 1001 };
+enum { T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_NVFP4 = 1001, T_FP8 = 1002 };
 
 static int32_t g_last_threads = 1;
 
@@ -66,6 +70,21 @@ double oracle_e4m3(uint8_t bits) {
     return sign ? -v : v;
 }
 
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 mantissa bits. */
+double oracle_bf16(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int f = bits & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* subnormal: f * 2^-126 / 128 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + f / 128.0, e - 127);
+    return sign ? -v : v;
+}
+
 /* OCP E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit. */
 double oracle_e2m1(uint8_t code) {
     int sign = (code >> 3) & 1;
@@ -82,6 +101,7 @@ int64_t oracle_row_bytes(int32_t type, int64_t k) {
     case T_Q5_K: return (k % 256) ? -1 : (k / 256) * 176;
     case T_Q6_K: return (k % 256) ? -1 : (k / 256) * 210;
     case T_NVFP4: return (k % 16) ? -1 : k / 2;
+    case T_FP8: return (k % 128) ? -1 : k;
     default: return -1;
     }
 }
@@ -148,6 +168,16 @@ static void dequant_nvfp4_row(const uint8_t *codes, const uint8_t *scales, int64
     }
 }
 
+/* One FP8 row: e4m3 code k times the bf16 scale of block (r / 128, k / 128);
+ * scales are [ceil(m/128)][k/128] little-endian bf16. */
+static void dequant_fp8_row(const uint8_t *codes, const uint8_t *scales, int64_t k, int64_t r, double *w) {
+    const uint8_t *srow = scales + (r / 128) * (k / 128) * 2;
+    for (int64_t i = 0; i < k; i++) {
+        const uint8_t *sp = srow + (i / 128) * 2;
+        w[i] = oracle_e4m3(codes[i]) * oracle_bf16((uint16_t)(sp[0] | (sp[1] << 8)));
+    }
+}
+
 /* Row r, exact, in fp64. */
 static void dequant_row(int32_t type, const uint8_t *data, const uint8_t *scales,
                         int64_t k, int64_t r, double *w) {
@@ -166,12 +196,15 @@ static void dequant_row(int32_t type, const uint8_t *data, const uint8_t *scales
     case T_NVFP4:
         dequant_nvfp4_row(row, scales + r * (k / 16), k, w);
         break;
+    case T_FP8:
+        dequant_fp8_row(row, scales, k, r, w);
+        break;
     }
 }
 
 static int check_args(int32_t type, const uint8_t *data, const uint8_t *scales, int64_t m, int64_t k) {
     if (!data || m < 1 || oracle_row_bytes(type, k) < 0) return -1;
-    if (type == T_NVFP4 && !scales) return -1;
+    if ((type == T_NVFP4 || type == T_FP8) && !scales) return -1;
     return 0;
 }
 

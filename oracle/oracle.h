@@ -8,7 +8,8 @@
  *
  * Type codes: 12 = Q4_K, 13 = Q5_K, 14 = Q6_K (the GGML type numbers the decode
  * GEMV page's typed-kernel template arguments <12>, <12,12>, <12,12,14> use),
- * 1001 = NVFP4 (this library's own code; the pages give none).
+ * 1001 = NVFP4 and 1002 = block-scaled FP8 (this library's own codes; the pages
+ * give none).
  *
  * Return values: 0 on success, -1 on a bad argument.
  */
@@ -24,6 +25,7 @@ extern "C" {
 double oracle_fp16(uint16_t bits);
 double oracle_e4m3(uint8_t bits);
 double oracle_e2m1(uint8_t code);
+double oracle_bf16(uint16_t bits);
 
 /* Bytes of one stored row (NVFP4: codes only). -1 if the type or k is invalid. */
 int64_t oracle_row_bytes(int32_t type, int64_t k);

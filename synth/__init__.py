@@ -13,6 +13,8 @@ Stored formats (byte offsets inside one 256-weight superblock, little-endian):
 * Q6_K, 210 B: 128 low-nibble bytes @0, 64 high-2-bit bytes @128, 16 int8
   scales @192, fp16 d @208.
 * NVFP4: codes [M][K/2] (two e2m1 codes per byte), scales [M][K/16] e4m3.
+* FP8 (block-scaled e4m3): codes [M][K] (one OCP E4M3FN code per byte), scales
+  [ceil(M/128)][K/128] bf16, one per 128-row x 128-column block.
 
 Value distributions follow the workload description of the decode-GEMV pages'
 Qwen3-4B Q4_K_M setting: fp16 d and dmin uniform in [1e-3, 2e-2]; the packed 6-bit
@@ -20,23 +22,28 @@ scale/min bytes uniform (every 6-bit field is then uniform in 0..63, because eac
 field is built from disjoint bits of independent uniform bytes); quant bytes
 uniform; Q6_K int8 scales uniform in 0..63; NVFP4 codes uniform over all 16 codes
 with e4m3 scales = round-to-nearest-even(uniform real in [0.01, 1]); x is
-fp16(N(0, 1)).
+fp16(N(0, 1)).  The FP8 format has no workload distribution in the pages; its
+codes are uniform over the 254 non-NaN e4m3 codes and its block scales are
+bf16(uniform real in [1e-3, 1e-2]).
 """
 from __future__ import annotations
 
 import numpy as np
 
-Q4_K, Q5_K, Q6_K, NVFP4 = 12, 13, 14, 1001
-TYPE_NAMES = {Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k", NVFP4: "nvfp4"}
+Q4_K, Q5_K, Q6_K, NVFP4, FP8 = 12, 13, 14, 1001, 1002
+TYPE_NAMES = {Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k", NVFP4: "nvfp4", FP8: "fp8_b128"}
 BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
 QK = 256          # weights per K-quant superblock
 NVFP4_GROUP = 16  # weights per NVFP4 scale
+FP8_BLOCK = 128   # rows and columns per FP8 scale block
 
 
 def row_bytes(wtype: int, k: int) -> int:
     """Bytes of one stored weight row (codes only for NVFP4)."""
     if wtype == NVFP4:
         return k // 2
+    if wtype == FP8:
+        return k
     return (k // QK) * BLOCK_BYTES[wtype]
 
 
@@ -96,6 +103,25 @@ def nvfp4_weights(m: int, k: int, rng: np.random.Generator, scale_range=(0.01, 1
     return codes, scales
 
 
+def bf16_bits(vals: np.ndarray) -> np.ndarray:
+    """Round reals to bfloat16 (nearest-even) and return the 16-bit patterns."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(vals, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def fp8_weights(m: int, k: int, rng: np.random.Generator, scale_range=(1e-3, 1e-2)):
+    """Random block-scaled FP8 weight matrix: (codes [m, k] u8 e4m3, scales
+    [ceil(m/128), k/128] as little-endian bf16 bytes, shape [ceil(m/128), k/64] u8)."""
+    if k % FP8_BLOCK:
+        raise ValueError("k must be a multiple of 128")
+    ok = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # no NaN codes
+    codes = ok[rng.integers(0, ok.size, size=(m, k))]
+    rb = (m + FP8_BLOCK - 1) // FP8_BLOCK
+    sb = bf16_bits(rng.uniform(*scale_range, size=(rb, k // FP8_BLOCK)))
+    return codes, np.ascontiguousarray(sb).view(np.uint8).reshape(rb, 2 * (k // FP8_BLOCK))
+
+
 def activations(n: int, k: int, rng: np.random.Generator) -> np.ndarray:
     """x as fp16 N(0, 1), shape [n, k]."""
     return rng.standard_normal(size=(n, k)).astype(np.float16)
@@ -105,6 +131,8 @@ def weights(wtype: int, m: int, k: int, rng: np.random.Generator, **kw):
     """(data, scales-or-None) for any supported type."""
     if wtype == NVFP4:
         return nvfp4_weights(m, k, rng, **kw)
+    if wtype == FP8:
+        return fp8_weights(m, k, rng, **kw)
     return kquant_weights(wtype, m, k, rng, **kw), None
 
 

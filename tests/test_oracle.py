@@ -41,6 +41,48 @@ def test_e4m3_decode_exhaustive(orc):
     assert orc.e4m3(0x7E) == 448.0         # largest finite
 
 
+def test_bf16_decode_exhaustive(orc):
+    import torch
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([orc.bf16(i) for i in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert orc.bf16(0x3F80) == 1.0 and orc.bf16(0x0001) == 2.0 ** -133
+
+
+def _fp8_grid():
+    """A 130 x 256 block-scaled FP8 matrix whose weights are written out by hand
+    (TandemLLM Kernels page, "FP8 matrix products": e4m3 codes, one bf16 scale per
+    128 x 128 block).  Every code is 0x38 (e4m3 1.0) except four in row 0."""
+    codes = np.full((130, 256), 0x38, dtype=np.uint8)
+    codes[0, :4] = [0x01, 0xFE, 0x7E, 0x80]           # 2^-9, -448, 448, -0
+    # bf16 scales: block (0,0) 0.25, (0,1) 2.0, (1,0) 0.5, (1,1) -4.0
+    scales = np.array([[0x3E80, 0x4000], [0x3F00, 0xC080]], dtype=np.uint16).view(np.uint8).reshape(2, 4)
+    want = np.empty((130, 256))
+    want[:128, :128], want[:128, 128:], want[128:, :128], want[128:, 128:] = 0.25, 2.0, 0.5, -4.0
+    want[0, :4] = [2.0 ** -11, -112.0, 112.0, -0.0]
+    return codes, scales, want
+
+
+def test_fp8_block_grid(orc):
+    codes, scales, want = _fp8_grid()
+    w = orc.dequant(synth.FP8, codes, scales, 130, 256)
+    assert np.array_equal(w, want.astype(np.float32))
+    assert np.signbit(w[0, 3])
+    assert np.array_equal(orc.dequant64(synth.FP8, codes, scales, 130, 256), want)
+    assert np.array_equal(orc.dequant(synth.FP8, codes, scales, 130, 256, r0=128, nr=2), want[128:].astype(np.float32))
+
+
+def test_fp8_products_exact_in_fp32(orc):
+    """e4m3 (4 significant bits) x bf16 (8): the fp32 weights are the exact ones."""
+    codes, scales = synth.fp8_weights(300, 512, synth.rng_for(78))
+    w64 = orc.dequant64(synth.FP8, codes, scales, 300, 512)
+    assert np.array_equal(orc.dequant(synth.FP8, codes, scales, 300, 512).astype(np.float64), w64)
+
+
 def test_e2m1_table(orc):
     # OCP MX e2m1 magnitudes for codes 0..7; bit 3 is the sign.
     table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
@@ -112,7 +154,7 @@ def test_block_and_row_stride(orc):
         assert np.array_equal(orc.dequant(t, mat, None, 2, 768, r0=1, nr=1)[0], want[1])
 
 
-@pytest.mark.parametrize("wtype", [12, 13, 14, 1001])
+@pytest.mark.parametrize("wtype", [12, 13, 14, 1001, 1002])
 def test_gemm_matches_numpy_fp64(orc, wtype):
     rng = synth.rng_for(123, wtype)
     m, k, n = 24, 768, 3
@@ -128,7 +170,7 @@ def test_gemm_matches_numpy_fp64(orc, wtype):
     assert np.array_equal(y2, y[:, rows]) and np.array_equal(a2, a[:, rows])
 
 
-@pytest.mark.parametrize("wtype", [12, 14, 1001])
+@pytest.mark.parametrize("wtype", [12, 14, 1001, 1002])
 def test_gemm_one_hot_returns_column(orc, wtype):
     rng = synth.rng_for(7, wtype)
     m, k = 16, 512
@@ -178,7 +220,7 @@ def test_generator_is_deterministic_and_in_range():
     assert sv.min() >= 0.0097 and sv.max() <= 1.0
 
 
-@pytest.mark.parametrize("wtype", [12, 13, 14, 1001])
+@pytest.mark.parametrize("wtype", [12, 13, 14, 1001, 1002])
 def test_dequant64_rounds_once_to_dequant(orc, wtype):
     """The fp32 weight is the exact weight rounded once (numpy's fp64 -> fp32
     conversion rounds to nearest even)."""

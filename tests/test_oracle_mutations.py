@@ -5,6 +5,7 @@ Each mutant is compiled with gcc into a temporary directory and checked against 
 same hand-derived golden blocks and the numpy fp64 matmul used by test_oracle.py.
 """
 import ctypes
+import importlib.util
 import json
 import os
 import subprocess
@@ -42,6 +43,9 @@ MUTANTS = {
     "e2m1_bias": ("ldexp(1.0 + 0.5 * f, e - 1)", "ldexp(1.0 + 0.5 * f, e)"),
     "fp16_subnormal_flush": ("v = ldexp((double)f, -24);", "v = 0.0;"),
     "gemm_reversed_x": ("acc += w[kk] * xt[kk];", "acc += w[kk] * xt[k - 1 - kk];"),
+    "fp8_scale_row_block": ("scales + (r / 128) * (k / 128) * 2", "scales + (r / 64) * (k / 128) * 2"),
+    "fp8_scale_col_block": ("srow + (i / 128) * 2", "srow + (i / 256) * 2"),
+    "bf16_bias": ("ldexp(1.0 + f / 128.0, e - 127)", "ldexp(1.0 + f / 128.0, e - 126)"),
     "gemm_unrounded_weights": ("for (int64_t kk = 0; kk < k; kk++) w[kk] = (float)w[kk];", ""),
     "q45_terms_in_fp32": ("w[p] = d * sc * q - dmin * mn;", "w[p] = (float)(d * sc * q) - (float)(dmin * mn);"),
     "gemm_transposed_out": ("y[t * nrows + i] = acc;", "y[i * n + t] = acc;"),
@@ -82,10 +86,21 @@ def _exact_block_ok(L):
     return np.array_equal(y[:, 0], out.astype(np.float32).astype(np.float64))
 
 
+def _fp8_grid_ok(L):
+    """The hand-written FP8 grid of test_oracle."""
+    spec = importlib.util.spec_from_file_location("t_oracle", os.path.join(ROOT, "tests", "test_oracle.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    codes, scales, want = mod._fp8_grid()
+    out = np.empty((130, 256), np.float32)
+    L.oracle_dequant(1002, codes.ctypes.data, scales.ctypes.data, 130, 256, 0, 130, out.ctypes.data)
+    return np.array_equal(out, want.astype(np.float32))
+
+
 def _pins_pass(L):
-    """True when every golden block, the exact-weight block and a numpy matmul
-    check agree with library L."""
-    if not _exact_block_ok(L):
+    """True when every golden block, the exact-weight block, the FP8 grid and a
+    numpy matmul check agree with library L."""
+    if not _exact_block_ok(L) or not _fp8_grid_ok(L):
         return False
     for fx in json.load(open(GOLDEN))["fixtures"]:
         data = np.frombuffer(bytes.fromhex(fx["data"]), np.uint8).copy()
@@ -96,7 +111,7 @@ def _pins_pass(L):
         for pos, val in fx["expect"].items():
             if out[int(pos)] != np.float32(val) or np.signbit(out[int(pos)]) != np.signbit(val):
                 return False
-    for wtype in (12, 13, 14, 1001):
+    for wtype in (12, 13, 14, 1001, 1002):
         rng = synth.rng_for(5, wtype)
         m, k, n = 8, 512, 3
         data, scales = synth.weights(wtype, m, k, rng)
