@@ -15,8 +15,9 @@ overhead is not part of the measurement.
 Headline: achieved HBM GB/s (algorithmic bytes / time) at N=1, the figure the
 decode-GEMV pages care about.  Beside it: a plain read of the same weight bytes
 (the read-stream probe, same rotation and call order), the same layer at N=32,
-the 512-token prefill GEMM in TFLOP/s, NVFP4 at 1/16/32 rows on 16384x8192 and
-the 151936x2560 head, and the CPU oracle on a bounded sample.
+the 512-token prefill GEMM in TFLOP/s, NVFP4 and block-scaled FP8 at 1/16/32
+rows on 16384x8192 and the 151936x2560 head, and the CPU oracle on a bounded
+sample.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -48,7 +49,11 @@ def kernel_source_sha() -> str:
 
 def call_bytes(wtype, m, k, n, resid=False):
     import synth
-    wb = m * synth.row_bytes(wtype, k) + (m * (k // 16) if wtype == synth.NVFP4 else 0)
+    wb = m * synth.row_bytes(wtype, k)
+    if wtype == synth.NVFP4:
+        wb += m * (k // 16)                                  # one e4m3 scale per 16 weights
+    elif wtype == synth.FP8:
+        wb += 2 * (-(-m // synth.FP8_BLOCK)) * (k // synth.FP8_BLOCK)   # bf16 per 128x128 block
     return wb + 2 * n * k + 4 * n * m + (4 * n * m if resid else 0)
 
 
@@ -216,23 +221,25 @@ def time_read_ceiling(layers, reps):
     return res
 
 
-NVFP4_SHAPES = (("nvfp4_16384x8192", 16384, 8192), ("nvfp4_151936x2560", 151936, 2560))
+LARGE_SHAPES = (("16384x8192", 16384, 8192), ("151936x2560", 151936, 2560))
 
 
-def time_nvfp4(reps=4):
-    """NVFP4 W4A16 at 1, 16 and 32 rows on the two large shapes (a 16384x8192
-    projection and the 151936x2560 output head), each rotated over enough distinct
-    copies to exceed 1 GiB so every call streams cold; one graph per (shape, n)."""
+def time_scaled(wtype, reps=4):
+    """A block-scaled format (NVFP4 W4A16 or FP8 W8A16) at 1, 16 and 32 rows on two
+    large shapes (a 16384x8192 projection and the 151936x2560 output head), each
+    rotated over enough distinct copies to exceed 1 GiB so every call streams cold;
+    one graph per (shape, n)."""
     import torch
     import gemm_q4_q5_amd as qg
     import synth
     res = {}
-    for i, (name, m, k) in enumerate(NVFP4_SHAPES):
-        data, scales = synth.weights(synth.NVFP4, m, k, synth.rng_for(4, i))
-        base = qg.QWeight.from_host(synth.NVFP4, data, m, k, scales, device="cuda")
+    for i, (name, m, k) in enumerate(LARGE_SHAPES):
+        data, scales = synth.weights(wtype, m, k, synth.rng_for(4, i) if wtype == synth.NVFP4
+                                     else synth.rng_for(5, wtype, i))
+        base = qg.QWeight.from_host(wtype, data, m, k, scales, device="cuda")
         wbytes = data.nbytes + scales.nbytes
         copies = max(2, -(-(1 << 30) // wbytes))
-        ws = [base] + [qg.QWeight(synth.NVFP4, base.data.clone(), m, k, base.scales.clone())
+        ws = [base] + [qg.QWeight(wtype, base.data.clone(), m, k, base.scales.clone())
                        for _ in range(copies - 1)]
         res[name] = {"copies": copies}
         for n in (1, 16, 32):
@@ -245,7 +252,7 @@ def time_nvfp4(reps=4):
                 for w in ws:
                     qg.qgemm_rows(w, x, y)
             us = 1000.0 * _time_graph(g, reps, 1) / (reps * copies)
-            b = call_bytes(synth.NVFP4, m, k, n)
+            b = call_bytes(wtype, m, k, n)
             res[name][f"n{n}"] = {"us": round(us, 2), "GB/s": round(b / (us * 1e3), 1),
                                   "pct_of_peak": round(100 * b / (us * 1e3) / PEAK_HBM_GBS, 2)}
             del g
@@ -395,6 +402,7 @@ def main():
     ap.add_argument("--no-n32", action="store_true", help="skip the N=32 pass")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-GEMM pass")
     ap.add_argument("--no-nvfp4", action="store_true", help="skip the NVFP4 large-shape pass")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 large-shape pass")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-stream ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel", choices=KERNELS, default=None,
@@ -483,7 +491,9 @@ def main():
     if not args.no_prefill:
         res["prefill_n512"] = time_prefill()
     if not args.no_nvfp4:
-        res["nvfp4_large"] = time_nvfp4()
+        res["nvfp4_large"] = time_scaled(qg.NVFP4)
+    if not args.no_fp8:
+        res["fp8_large"] = time_scaled(qg.FP8)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res))

@@ -15,7 +15,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemm.so")
 
-Q4_K, Q5_K, Q6_K, NVFP4 = 12, 13, 14, 1001
+Q4_K, Q5_K, Q6_K, NVFP4, FP8 = 12, 13, 14, 1001, 1002
 MAX_ROWS = 32
 STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_SHAPE", -3: "QG_ERR_ROWS",
           -4: "QG_ERR_TYPE", -5: "QG_ERR_ALIGN", -6: "QG_ERR_LAUNCH"}
@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
             "qgemv_q5k": ([p, p, fp, i64, i64, p], ctypes.c_int),
             "qgemv_q6k": ([p, p, fp, i64, i64, p], ctypes.c_int),
             "qgemv_nvfp4": ([p, p, p, fp, i64, i64, p], ctypes.c_int),
+            "qgemv_fp8": ([p, p, p, fp, i64, i64, p], ctypes.c_int),
             "qgemm_rows": ([W, p, fp, i32, p], ctypes.c_int),
             "qgemv_add": ([W, p, fp, fp, i32, p], ctypes.c_int),
             "qgemv_pair": ([W, W, p, fp, fp, i32, p], ctypes.c_int),
@@ -86,7 +87,7 @@ class QWeight:
     data: "object"                 # torch.uint8 tensor [m, row_bytes]
     m: int
     k: int
-    scales: Optional[object] = None  # NVFP4 e4m3 bytes [m, k/16]
+    scales: Optional[object] = None  # NVFP4 e4m3 bytes [m, k/16]; FP8 bf16 [ceil(m/128), k/128]
 
     def c(self) -> CWeight:
         return CWeight(self.type, 0, self.data.data_ptr(),
@@ -144,9 +145,15 @@ def qgemv_nvfp4(w: QWeight, x, y=None):
     return y
 
 
+def qgemv_fp8(w: QWeight, x, y=None):
+    y = _out((w.m,), x, y)
+    _check(lib().qgemv_fp8(_ptr(w.data), _ptr(w.scales), _ptr(x), _ptr(y), w.m, w.k, _stream()))
+    return y
+
+
 def qgemv(w: QWeight, x, y=None):
     """The single-token GEMV entry point of w's type."""
-    f = {Q4_K: qgemv_q4k, Q5_K: qgemv_q5k, Q6_K: qgemv_q6k, NVFP4: qgemv_nvfp4}[w.type]
+    f = {Q4_K: qgemv_q4k, Q5_K: qgemv_q5k, Q6_K: qgemv_q6k, NVFP4: qgemv_nvfp4, FP8: qgemv_fp8}[w.type]
     return f(w, x, y)
 
 

@@ -36,7 +36,8 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-bool known_type(int32_t t) { return t == QG_Q4_K || t == QG_Q5_K || t == QG_Q6_K || t == QG_NVFP4; }
+bool known_type(int32_t t) { return t == QG_Q4_K || t == QG_Q5_K || t == QG_Q6_K || t == QG_NVFP4 || t == QG_FP8; }
+bool has_scales(int32_t t) { return t == QG_NVFP4 || t == QG_FP8; }
 
 const char *type_name(int32_t t) {
     switch (t) {
@@ -44,6 +45,7 @@ const char *type_name(int32_t t) {
     case QG_Q5_K: return "Q5_K";
     case QG_Q6_K: return "Q6_K";
     case QG_NVFP4: return "NVFP4";
+    case QG_FP8: return "FP8";
     default: return "?";
     }
 }
@@ -58,13 +60,13 @@ int check_weight(const qg_weight *w, const char *name) {
     if (!known_type(w->type)) return fail(QG_ERR_TYPE, "%s: unknown type %d", name, w->type);
     if (w->reserved != 0) return fail(QG_ERR_TYPE, "%s: reserved field must be 0", name);
     if (!w->data) return fail(QG_ERR_NULL, "%s: data is NULL", name);
-    if (w->type == QG_NVFP4 && !w->scales) return fail(QG_ERR_NULL, "%s: NVFP4 scales are NULL", name);
+    if (has_scales(w->type) && !w->scales) return fail(QG_ERR_NULL, "%s: %s scales are NULL", name, type_name(w->type));
     if (w->m < 1 || w->m > kMaxM) return fail(QG_ERR_SHAPE, "%s: m = %lld out of range", name, (long long)w->m);
     if (w->k < 256 || w->k > kMaxK || w->k % 256)
         return fail(QG_ERR_SHAPE, "%s: k = %lld must be a positive multiple of 256 (<= %lld)", name,
                     (long long)w->k, (long long)kMaxK);
     if (!aligned(w->data, 16)) return fail(QG_ERR_ALIGN, "%s: data is not 16-byte aligned", name);
-    if (w->type == QG_NVFP4 && !aligned(w->scales, 16))
+    if (has_scales(w->type) && !aligned(w->scales, 16))
         return fail(QG_ERR_ALIGN, "%s: scales are not 16-byte aligned", name);
     return QG_OK;
 }
@@ -238,6 +240,7 @@ int64_t qg_row_bytes(int32_t type, int64_t k) {
     case QG_Q5_K: return k / 256 * 176;
     case QG_Q6_K: return k / 256 * 210;
     case QG_NVFP4: return k / 2;
+    case QG_FP8: return k;
     default: return -1;
     }
 }
@@ -269,6 +272,10 @@ int qgemv_q6k(const void *w, const void *x, float *y, int64_t m, int64_t k, void
 int qgemv_nvfp4(const void *codes, const void *scales, const void *x, float *y, int64_t m, int64_t k,
                 void *stream) {
     return gemv_single(QG_NVFP4, codes, scales, x, y, m, k, stream);
+}
+int qgemv_fp8(const void *codes, const void *scales, const void *x, float *y, int64_t m, int64_t k,
+              void *stream) {
+    return gemv_single(QG_FP8, codes, scales, x, y, m, k, stream);
 }
 
 int qgemm_rows(const qg_weight *w, const void *x, float *y, int32_t n, void *stream) {

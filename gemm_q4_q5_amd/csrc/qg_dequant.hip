@@ -55,6 +55,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs A) {
                 out[pos + 3] = coef[g] * (f16hi(o.v[g][1]) - bias);
             }
         }
+    } else if (A.type == T_FP8) {
+        const RawF8 R = Loader<T_FP8>::load(A.data, A.scales, A.row_bytes, r, (int)b, c);
+        const float sc = bf16_lo(R.sc);
+        const uint32_t qw[16] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w,
+                                 R.q2.x, R.q2.y, R.q2.z, R.q2.w, R.q3.x, R.q3.y, R.q3.z, R.q3.w};
+        for (int i = 0; i < 16; ++i)
+            for (int e = 0; e < 4; ++e) out[64 * c + 4 * i + e] = e4m3_at(qw[i], e) * sc;   // exact
     } else {
         const RawF4 R = load_f4(A.data + r * A.row_bytes + b * 128,
                                 A.scales + r * (A.row_bytes / 8) + b * 16, c);

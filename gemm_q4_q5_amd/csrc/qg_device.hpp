@@ -29,7 +29,7 @@ namespace qg {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-enum : int { T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_NVFP4 = 1001 };
+enum : int { T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_NVFP4 = 1001, T_FP8 = 1002 };
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -204,6 +204,17 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, int byte) {
     }
     return as_u32(v);
 }
+
+// OCP E4M3FN codes: bytes 0, 1 (hi = false) or 2, 3 (hi = true) of w -> fp16 pair,
+// lower byte in the low half (exact: every e4m3 value is an fp16 value).
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w, bool hi) {
+    return as_u32(hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+
+// bf16 bits (the low 16 bits of u) -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
 // OCP E4M3FN byte `byte` of w -> fp32 (exact).
 __device__ __forceinline__ float e4m3_at(uint32_t w, int byte) {

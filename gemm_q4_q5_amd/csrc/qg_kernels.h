@@ -8,10 +8,10 @@ namespace qg {
 enum : int { MODE_PLAIN = 0, MODE_SWIGLU = 1 };
 
 // Weight-type sets a kernel instantiation handles.
-enum : int { TS_Q4 = 1, TS_Q5 = 2, TS_Q6 = 4, TS_F4 = 8, TS_ALL = 15 };
+enum : int { TS_Q4 = 1, TS_Q5 = 2, TS_Q6 = 4, TS_F4 = 8, TS_F8 = 16, TS_ALL = 31 };
 
 constexpr __host__ __device__ int type_bit(int type) {
-    return type == 12 ? TS_Q4 : type == 13 ? TS_Q5 : type == 14 ? TS_Q6 : TS_F4;
+    return type == 12 ? TS_Q4 : type == 13 ? TS_Q5 : type == 14 ? TS_Q6 : type == 1001 ? TS_F4 : TS_F8;
 }
 
 struct DequantArgs {

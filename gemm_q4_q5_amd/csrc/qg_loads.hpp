@@ -2,7 +2,8 @@
 // dequant probe (qg_dequant.hip) and the dequantizing stage of the prefill GEMM
 // (qg_prefill.hip).  Chunk c of a K-quant superblock is quant bytes 32c .. 32c+31
 // (sub-blocks 2c and 2c+1); for Q6_K it is half c >> 1, positions 16(c & 1) ..
-// 16(c & 1)+15 of each of its four 32-weight groups; for NVFP4, codes 64c .. 64c+63.
+// 16(c & 1)+15 of each of its four 32-weight groups; for NVFP4 and FP8, codes
+// 64c .. 64c+63 (FP8: with the bf16 scale of the 128-wide block they sit in).
 #pragma once
 #include "qg_device.hpp"
 #include "qg_kernels.h"
@@ -87,6 +88,22 @@ __device__ __forceinline__ RawQ6 load_q6(const uint8_t *blk, int c) {
     return r;
 }
 
+struct RawF8 {
+    uint4 q0, q1, q2, q3;
+    uint32_t sc;   // bf16 scale in the low 16 bits
+};
+
+// codes: the superblock's 256 codes; srow: the row's bf16 scale row; b: superblock.
+__device__ __forceinline__ RawF8 load_f8(const uint8_t *codes, const uint8_t *srow, int b, int c) {
+    RawF8 r;
+    r.q0 = ld16(codes + 64 * c);
+    r.q1 = ld16(codes + 64 * c + 16);
+    r.q2 = ld16(codes + 64 * c + 32);
+    r.q3 = ld16(codes + 64 * c + 48);
+    r.sc = *reinterpret_cast<const uint16_t *>(srow + (2 * b + (c >> 1)) * 2);
+    return r;
+}
+
 __device__ __forceinline__ RawF4 load_f4(const uint8_t *codes, const uint8_t *scales, int c) {
     RawF4 r;
     r.q0 = ld16(codes + 32 * c);
@@ -133,6 +150,15 @@ struct Loader<T_NVFP4> {
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *scales, int64_t row_bytes,
                                                int64_t r, int b, int c) {
         return load_f4(data + r * row_bytes + (int64_t)b * 128, scales + r * (row_bytes / 8) + (int64_t)b * 16, c);
+    }
+};
+
+template <>
+struct Loader<T_FP8> {
+    typedef RawF8 Raw;
+    static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *scales, int64_t row_bytes,
+                                               int64_t r, int b, int c) {
+        return load_f8(data + r * row_bytes + (int64_t)b * 256, scales + (r >> 7) * (row_bytes / 64), b, c);
     }
 };
 

@@ -77,6 +77,13 @@ struct MRawF4 {
     uint4 q0, q1;
     uint32_t sc;
 };
+// Block-scaled FP8: the lane's 32 codes of each 128-wide scale block of the
+// superblock (bytes 32g .. 32g+31 of block 0 in a0/a1, of block 1 in b0/b1) and the
+// two blocks' bf16 scales (block 0 low).
+struct MRawF8 {
+    uint4 a0, a1, b0, b1;
+    uint32_t sc;
+};
 
 __device__ __forceinline__ uint4 mld16(const uint8_t *p) {
     const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
@@ -95,6 +102,10 @@ struct MRawOf<T_Q6_K> {
 template <>
 struct MRawOf<T_NVFP4> {
     typedef MRawF4 type;
+};
+template <>
+struct MRawOf<T_FP8> {
+    typedef MRawF8 type;
 };
 
 // Q6_K blocks sit at 210-byte offsets, so a block may start 2 bytes past a 4-byte
@@ -134,6 +145,13 @@ __device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, co
         r.s1 = s01.y;
         r.s2 = mld4(mis ? ps + 8 : ps + 4);
         r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+    } else if constexpr (T == T_FP8) {
+        const uint8_t *c = row + (int64_t)b * 256 + 32 * g;
+        r.a0 = mld16(c);
+        r.a1 = mld16(c + 16);
+        r.b0 = mld16(c + 128);
+        r.b1 = mld16(c + 144);
+        r.sc = mld4(srow + (int64_t)b * 4);   // scale row of the lane's 128-row block
     } else {
         const uint8_t *c = row + (int64_t)b * 128;
         r.q0 = mld16(c + 32 * g);
@@ -174,6 +192,8 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_m
 //   Q4_K/Q5_K: 64g + {4s, 4s+2, 4s+1, 4s+3, 32+4s, 34+4s, 33+4s, 35+4s}
 //   Q6_K:      128(g >> 1) + 16(g & 1) + 4(s >> 1) + 64(s & 1) + {0..3, 32..35}
 //   NVFP4:     64g + 8s + 0..7
+//   FP8:       128(s >> 2) + 32g + 8(s & 3) + 0..7   (steps 0..3 and 4..7 each stay
+//              inside one 128-wide scale block)
 constexpr int kUnitsPerTok = 9;
 constexpr int kZeroUnits = 9;
 
@@ -184,6 +204,9 @@ __device__ __forceinline__ void slot_pieces(int g, int s, int &o0, int &o1) {
         o1 = o0 + 32;
     } else if constexpr (T == T_NVFP4) {
         o0 = 64 * g + 8 * s;
+        o1 = o0 + 4;
+    } else if constexpr (T == T_FP8) {
+        o0 = 128 * (s >> 2) + 32 * g + 8 * (s & 3);
         o1 = o0 + 4;
     } else {
         o0 = 64 * g + 4 * s;
@@ -204,13 +227,14 @@ template <int T>
 __device__ __forceinline__ int xhalf_base(int g, int h) {
     if constexpr (T == T_Q6_K) return 128 * (g >> 1) + 16 * (g & 1) + 8 * h;
     else if constexpr (T == T_NVFP4) return 64 * g + 32 * h;
+    else if constexpr (T == T_FP8) return 128 * h + 32 * g;
     else return 64 * g + 16 * h;
 }
 // Loads at base + {0, 8, 32, 40} (Q4_K/Q5_K), {0, 64, 32, 96} (Q6_K), {0, 8, 16, 24} (NVFP4).
 template <int T>
 __device__ __forceinline__ int xhalf_off(int l) {
     if constexpr (T == T_Q6_K) return (l & 1) * 64 + (l >> 1) * 32;
-    else if constexpr (T == T_NVFP4) return 8 * l;
+    else if constexpr (T == T_NVFP4 || T == T_FP8) return 8 * l;
     else return (l & 1) * 8 + (l >> 1) * 32;
 }
 template <int T>
@@ -220,7 +244,7 @@ __device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
     if constexpr (T == T_Q6_K) {
         v = X.v[2 * e + (i & 1)];
         hi = i >> 1;
-    } else if constexpr (T == T_NVFP4) {
+    } else if constexpr (T == T_NVFP4 || T == T_FP8) {
         v = X.v[i];
         hi = e;
     } else {
@@ -387,6 +411,14 @@ __device__ __forceinline__ h8 f4_step(const MRawF4 &R, int s) {
                  pk_mul(fp4_pair(qw[s], 3), S));
 }
 
+// FP8 step s: the lane's codes 8(s & 3) .. 8(s & 3) + 7 of scale block s >> 2 (exact
+// fp16); the block's bf16 scale is applied in fp32 after its four MFMAs.
+__device__ __forceinline__ h8 f8_step(const MRawF8 &R, int s) {
+    const uint4 v = (s >> 2) ? ((s & 2) ? R.b1 : R.b0) : ((s & 2) ? R.a1 : R.a0);
+    const uint32_t w0 = (s & 1) ? v.z : v.x, w1 = (s & 1) ? v.w : v.y;
+    return mk_h8(fp8_pair(w0, false), fp8_pair(w0, true), fp8_pair(w1, false), fp8_pair(w1, true));
+}
+
 template <int I, int NG>
 __device__ __forceinline__ void q6_dword(const MRawQ6 &R, const Q6Tile &K, const uint4 *const (&xv)[NG], f4 (&c1)[NG]) {
     h8 b0, b1;
@@ -450,6 +482,27 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(K.d, c1[q][e], acc[i][q][e]);
         }
+    } else if constexpr (T == T_FP8) {
+        // c = sum over one 128-wide scale block of code*x; y += scale*c per block.
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f4 c1[NG];
+#pragma unroll
+                for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 4 * h; s < 4 * h + 4; ++s) {
+                    const h8 b = f8_step(R[i], s);
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
+                }
+                const float sc = h ? bf16_hi(R[i].sc) : bf16_lo(R[i].sc);
+#pragma unroll
+                for (int q = 0; q < NG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(sc, c1[q][e], acc[i][q][e]);
+            }
     } else {
 #pragma unroll
         for (int i = 0; i < NT; ++i)
@@ -645,7 +698,11 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT>())) void mma_ke
         const int64_t r = rows[i] < S.m ? rows[i] : S.m - 1;   // rows past m read row m-1; results dropped
         const bool second = two_mats && i == 1;
         wr[i] = (second ? S.data2 : S.data) + r * S.row_bytes;
-        sr[i] = S.type == T_NVFP4 ? (second ? S.scales2 : S.scales) + r * (S.row_bytes / 8) : nullptr;
+        const uint8_t *sc = second ? S.scales2 : S.scales;
+        // NVFP4: one e4m3 scale per 16 weights of the row; FP8: the bf16 scale row
+        // of the row's 128-row block (K/128 scales of 2 bytes).
+        sr[i] = S.type == T_NVFP4 ? sc + r * (S.row_bytes / 8)
+                                  : (S.type == T_FP8 ? sc + (r >> 7) * (S.row_bytes / 64) : nullptr);
     }
     f4 acc[NT][NG];
 #pragma unroll
@@ -660,6 +717,8 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT>())) void mma_ke
         mma_body<T_Q6_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
     else if ((TS & TS_F4) && S.type == T_NVFP4)
         mma_body<T_NVFP4, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+    else if ((TS & TS_F8) && S.type == T_FP8)
+        mma_body<T_FP8, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
 
     // Partials of the KS waves of a row tile, added in wave order.
     if (KS > 1) {

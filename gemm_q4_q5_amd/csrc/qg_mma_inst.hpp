@@ -23,6 +23,7 @@ static hipError_t launch_ts(const MmaArgs &A, int ts, int grid, size_t lds, hipS
     case TS_Q5: return launch_one<TS_Q5, NG, WV, NT, SW>(A, grid, lds, st);
     case TS_Q6: return launch_one<TS_Q6, NG, WV, NT, SW>(A, grid, lds, st);
     case TS_F4: return launch_one<TS_F4, NG, WV, NT, SW>(A, grid, lds, st);
+    case TS_F8: return launch_one<TS_F8, NG, WV, NT, SW>(A, grid, lds, st);
     default:
         if constexpr (SW) return hipErrorInvalidValue;   // SwiGLU pairs share one type
         else if (ts == (TS_Q4 | TS_Q6)) return launch_one<TS_Q4 | TS_Q6, NG, WV, NT, false>(A, grid, lds, st);

@@ -105,6 +105,20 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
             d[0] = make_uint4(out[g][0], out[g][1], out[g][2], out[g][3]);
             d[1] = make_uint4(out[g][4], out[g][5], out[g][6], out[g][7]);
         }
+    } else if (T == T_FP8) {
+        // FP8 chunk c: 64 codes at step offsets 64hf + 0..63; code * scale is exact in
+        // fp32 (4 + 8 significant bits) and rounded once to fp16.
+        const RawF8 &Q = reinterpret_cast<const RawF8 &>(R);
+        const float sc = bf16_lo(Q.sc);
+        const uint32_t qw[16] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w,
+                                 Q.q2.x, Q.q2.y, Q.q2.z, Q.q2.w, Q.q3.x, Q.q3.y, Q.q3.z, Q.q3.w};
+        uint4 *d = reinterpret_cast<uint4 *>(wrow + 64 * hf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t a = qw[2 * i], b = qw[2 * i + 1];
+            d[i] = make_uint4(pack_h2(e4m3_at(a, 0) * sc, e4m3_at(a, 1) * sc), pack_h2(e4m3_at(a, 2) * sc, e4m3_at(a, 3) * sc),
+                              pack_h2(e4m3_at(b, 0) * sc, e4m3_at(b, 1) * sc), pack_h2(e4m3_at(b, 2) * sc, e4m3_at(b, 3) * sc));
+        }
     } else {
         // NVFP4 chunk c: 64 codes at step offsets 64hf + 0..63, four scales
         const RawF4 &Q = reinterpret_cast<const RawF4 &>(R);
@@ -225,6 +239,7 @@ hipError_t launch_prefill(const PrefillArgs &A, int bm, int bn, hipStream_t st) 
     case T_Q4_K: return launch_t<T_Q4_K>(A, bm, bn, st);
     case T_Q5_K: return launch_t<T_Q5_K>(A, bm, bn, st);
     case T_Q6_K: return launch_t<T_Q6_K>(A, bm, bn, st);
+    case T_FP8: return launch_t<T_FP8>(A, bm, bn, st);
     default: return launch_t<T_NVFP4>(A, bm, bn, st);
     }
 }

@@ -70,12 +70,14 @@ extern "C" {
 
 /* Tensor type codes.  12 and 14 are the GGML type numbers of Q4_K and Q6_K that
  * [PF] Path C's typed kernels are instantiated with (<12>, <12,12>, <12,12,14>);
- * 13 (Q5_K) sits between them; NVFP4 has no GGML number and takes 1001. */
+ * 13 (Q5_K) sits between them; NVFP4 and block-scaled FP8 have no GGML number and
+ * take 1001 and 1002. */
 typedef enum {
     QG_Q4_K = 12,
     QG_Q5_K = 13,
     QG_Q6_K = 14,
-    QG_NVFP4 = 1001
+    QG_NVFP4 = 1001,
+    QG_FP8 = 1002   /* [TK] "FP8 matrix products": e4m3 codes, one bf16 scale per 128x128 block */
 } qg_type;
 
 /* Status codes. */
@@ -89,19 +91,21 @@ typedef enum {
 
 #define QG_MAX_ROWS 32       /* largest n of the row-invariant calls ([KN] GEMM_MAX_BATCH) */
 
-/* A quantized weight matrix (m rows of k weights).  `scales` is used by NVFP4
- * only and must be NULL-free for it; it is ignored for the K-quants. */
+/* A quantized weight matrix (m rows of k weights).  `scales` is used by NVFP4 and
+ * FP8 and must be non-NULL (16-byte aligned) for them; it is ignored for the
+ * K-quants.  FP8: data = e4m3 codes [m][k] (OCP E4M3FN, one byte per weight), scales
+ * = bf16 [ceil(m/128)][k/128] row-major, weight (r, c) = code * scale[r/128][c/128]. */
 typedef struct qg_weight {
     int32_t type;        /* a qg_type                                   */
     int32_t reserved;    /* must be 0                                   */
-    const void *data;    /* superblocks, or NVFP4 codes                 */
-    const void *scales;  /* NVFP4 e4m3 scales [m][k/16]; else unused    */
+    const void *data;    /* superblocks, or NVFP4 / FP8 codes           */
+    const void *scales;  /* NVFP4 e4m3 [m][k/16]; FP8 bf16 [m/128][k/128] */
     int64_t m;           /* rows (output features)                      */
     int64_t k;           /* columns (reduction length)                  */
 } qg_weight;
 
-/* Bytes of one stored weight row (NVFP4: of the codes only); -1 if the type is
- * unknown or k is not a multiple of 256. */
+/* Bytes of one stored weight row (NVFP4 and FP8: of the codes only); -1 if the
+ * type is unknown or k is not a multiple of 256. */
 int64_t qg_row_bytes(int32_t type, int64_t k);
 
 /* Static text for a status code. */
@@ -120,6 +124,14 @@ const char *qg_last_error(void);
 int qgemv_q4k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream);
 int qgemv_q5k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream);
 int qgemv_q6k(const void *w, const void *x, float *y, int64_t m, int64_t k, void *stream);
+
+/* Block-scaled FP8 W8A16 GEMV ([TK] FP8 matrix products: the checkpoint's e4m3
+ * codes with one bf16 scale per 128 x 128 block, read as stored): codes [m][k],
+ * scales bf16 [ceil(m/128)][k/128], x fp16 [k], y fp32 [m].  k a multiple of 256.
+ * Each 128-wide block's sum of code*x is formed on the matrix cores (codes exact in
+ * fp16) and scaled in fp32; row-invariant like every other type. */
+int qgemv_fp8(const void *codes, const void *scales, const void *x, float *y, int64_t m, int64_t k,
+              void *stream);
 
 /* NVFP4 W4A16 GEMV ([TK] NVFP4 matrix products): codes [m][k/2], scales e4m3
  * [m][k/16], x fp16 [k], y fp32 [m]. */

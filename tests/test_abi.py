@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("qgemv_q4k", "qgemv_q5k", "qgemv_q6k", "qgemv_nvfp4", "qgemm_rows", "qgemv_add",
+    for want in ("qgemv_q4k", "qgemv_q5k", "qgemv_q6k", "qgemv_nvfp4", "qgemv_fp8", "qgemm_rows", "qgemv_add",
                  "qgemv_pair", "qgemv_triple", "qgemv_pair_swiglu", "qdequant", "qg_row_bytes",
                  "qg_status_str", "qg_last_error"):
         assert want in names
@@ -39,6 +39,7 @@ def test_row_bytes():
     assert qg.row_bytes(qg.Q5_K, 9728) == 38 * 176
     assert qg.row_bytes(qg.Q6_K, 9728) == 38 * 210
     assert qg.row_bytes(qg.NVFP4, 8192) == 4096
+    assert qg.row_bytes(qg.FP8, 2560) == 2560
     assert qg.row_bytes(qg.Q4_K, 100) == -1
     assert qg.row_bytes(99, 256) == -1
 
@@ -67,6 +68,9 @@ def w(type_=12, data=FAKE, scales=None, m=8, k=512, reserved=0):
     (dict(data=FAKE + 4), -5),
     (dict(type_=1001, scales=None), -1),
     (dict(type_=1001, scales=FAKE + 8), -5),
+    (dict(type_=1002, scales=None), -1),
+    (dict(type_=1002, scales=FAKE + 8), -5),
+    (dict(type_=1002, scales=FAKE, k=384), -2),
 ])
 def test_rows_validation(case, code):
     L = qg.lib()
@@ -92,6 +96,8 @@ def test_gemv_single_validation():
     assert L.qgemv_q5k(FAKE, FAKE, FAKE, 8, 500, None) == -2
     assert L.qgemv_q6k(FAKE, FAKE, FAKE, 0, 512, None) == -2
     assert L.qgemv_nvfp4(FAKE, None, FAKE, FAKE, 8, 512, None) == -1
+    assert L.qgemv_fp8(FAKE, None, FAKE, FAKE, 8, 512, None) == -1
+    assert L.qgemv_fp8(FAKE, FAKE, FAKE, FAKE, 8, 640, None) == -2
     assert L.qgemv_q4k(FAKE, FAKE + 8, FAKE, 8, 512, None) == -5
 
 

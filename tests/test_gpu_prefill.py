@@ -17,7 +17,7 @@ from gpu_util import assert_within, bits, device, weight, x_dev
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4]
+TYPES = [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4, qg.FP8]
 
 
 @pytest.mark.parametrize("wt", TYPES)
