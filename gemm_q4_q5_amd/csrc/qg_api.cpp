@@ -125,37 +125,70 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     a.n = n;
     a.mode = mode;
     a.nt = fuse2 ? 2 : 1;
-    // Workgroups of at least four waves; KS waves per row tile.
-    int wv0 = 4;
+    // K phases of each matrix (fixed by its shape: the arithmetic of every row);
+    // every matrix's, also the second of a pair served by the same waves.
     int ks[3] = {1, 1, 1};
-    for (int s = 0; s < a.nseg; ++s) {
+    int ksmax = 1, ksmin = 16;
+    for (int s = 0; s < nseg; ++s) {
         ks[s] = choose_ks(w[s]->type, w[s]->m, k);
-        wv0 = std::max(wv0, ks[s]);
+        ksmax = std::max(ksmax, ks[s]);
+        ksmin = std::min(ksmin, ks[s]);
     }
-    if (!sw && a.nt == 2 && wv0 > 8) {   // a plain pair takes two tiles per wave only up to 8 waves
+    if (!sw && a.nt == 2 && ksmax > 8) {   // a plain pair takes two tiles per wave only up to 8 waves
         a.nt = 1;
         a.nseg = 2;
     }
     const int ng = n > 16 ? 2 : 1;
     const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
-    // Decode path (each wave stages its own x) where a wave's superblocks fit one
-    // round of loads and their x one staging half-group per lane.
+    // Decode path (each wave stages its own x, one phase per wave) where a wave's
+    // superblocks fit one round of loads and their x one staging half-group per lane.
     const int depth = a.nt == 2 ? 2 : qg::kMmaDepth;
     auto dec_ok = [&](int s, int wv) {
         const int maxcnt = (a.nb + ks[s] - 1) / ks[s];
         const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
         return maxcnt <= depth && 8 * n * maxcnt <= 64 * qg::kMmaDecRounds && need <= kMmaLdsBudget;
     };
+    bool any_dec = false;
+    for (int s = 0; s < a.nseg; ++s) any_dec = any_dec || dec_ok(s, std::max(4, ksmax));
+    // Phases per wave (np).  Only the number of waves serving a tile changes with it,
+    // never a row's arithmetic, so it may follow n.  A wave with np phases streams
+    // np times the superblocks and a workgroup serves np times the rows, which
+    // shares each staged chunk of x among more rows.  Taken where the launch keeps
+    // enough waves: at least 4096 (16 per CU) below 8 tokens, where the decode path
+    // (np = 1) stays whenever its workgroups are at most 8 waves; at least 1216 from
+    // 8 tokens on.  Measured on cold rotations (us per call, np 1 -> chosen):
+    // 16384x8192 FP8 at 1 / 32 tokens 38 -> 28 / 129 -> 46; the 151936x2560 Q4_K
+    // head at 8 / 32 tokens 100 -> 61 / 138 -> 86; 9728x2560 Q4_K at 32 tokens 19.5 -> 13.5.
+    int64_t waves1 = 0;   // waves at one phase per wave
+    for (int s = 0; s < a.nseg; ++s) waves1 += (w[s]->m + 15) / 16 * ks[s];
+    bool one_type = true;
+    for (int s = 1; s < nseg; ++s) one_type = one_type && w[s]->type == w[0]->type;
+    int np = 1;
+    if (one_type && !(n < 8 && any_dec && ksmax <= 8)) {
+        const int64_t want = n < 8 ? 4096 : 1216;
+        for (int p = a.nt == 2 ? 2 : 4; p >= 2; p /= 2)
+            if (ksmin >= p && waves1 / p >= want) {
+                np = p;
+                break;
+            }
+    }
+    a.np = np;
+    int kw[3] = {1, 1, 1};   // waves per row tile
+    int kwmax = 1;
+    for (int s = 0; s < a.nseg; ++s) {
+        kw[s] = ks[s] / np;
+        kwmax = std::max(kwmax, kw[s]);
+    }
+    if (np > 1) any_dec = false;
+    const int wv0 = std::max(4, kwmax);   // workgroups of at least four waves
     auto grid_of = [&](int wv) {
         int gr = 0;
         for (int s = 0; s < a.nseg; ++s) {
-            const int64_t rows_per_wg = 16 * (wv / ks[s]);
+            const int64_t rows_per_wg = 16 * (wv / kw[s]);
             gr += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
         }
         return gr;
     };
-    bool any_dec = false;
-    for (int s = 0; s < a.nseg; ++s) any_dec = any_dec || dec_ok(s, wv0);
     // The general path stages x per workgroup in chunks of kc superblocks, and each
     // chunk change costs a round of x loads behind the weight stream.  A grid of about
     // one workgroup per CU (256 CUs) may take all of the CU's LDS for fewer, larger
@@ -194,7 +227,7 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
             g.scales2 = (const uint8_t *)w[1]->scales;
             g.y2 = sw ? nullptr : y[1];
         }
-        const int64_t rows_per_wg = 16 * (wv / ks[s]);
+        const int64_t rows_per_wg = 16 * (wv / kw[s]);
         grid += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
     }
     const size_t budget = grid <= kOneRound ? kMmaLdsMax : kMmaLdsBudget;
@@ -202,15 +235,16 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     a.kc = std::min(kc, a.nb);
     size_t lds = kMmaZeroBytes;
     for (int s = 0; s < a.nseg; ++s) {
-        if (dec_ok(s, wv)) {
+        if (np == 1 && dec_ok(s, wv)) {
             a.seg[s].dec = 1;
             lds = std::max(lds, kMmaZeroBytes + (size_t)wv * ((a.nb + ks[s] - 1) / ks[s]) * per_sb);
         } else {   // the general path's x chunk
             lds = std::max(lds, kMmaZeroBytes + per_sb * a.kc);
         }
     }
-    const size_t part = (size_t)wv * 64 * 4 * (4 * ng * a.nt);   // partial sums of the K split
-    lds = std::max(lds, part);
+    // Partial sums of the K phases: a slot per phase and tile group, where a tile has
+    // more than one wave.
+    if (kwmax > 1) lds = std::max(lds, (size_t)wv * np * 1024 * ng * a.nt);
     int ts = 0;
     for (int s = 0; s < nseg; ++s) ts |= qg::type_bit(w[s]->type);
     hipError_t e = qg::launch_mma(a, ts, grid, lds, (hipStream_t)stream);

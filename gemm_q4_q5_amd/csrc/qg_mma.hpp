@@ -8,9 +8,12 @@
 // wide loads into operand registers, so 1..16 rows cost one instruction per weight
 // tile and 17..32 rows two).
 //
-// Work split.  A wave owns a tile of 16 weight rows and every KS-th superblock of
-// K (superblocks kp, kp + KS, ...); the KS waves of a tile sit in one workgroup and
-// their partial sums are added in wave order.  KS depends only on (type, m, k).
+// Work split.  K of a tile of 16 weight rows is split into KS phases, phase p
+// summing superblocks p, p + KS, ... in increasing order, and the phases' partial
+// sums are added in phase order; KS depends only on (type, m, k).  A wave computes
+// NP phases, every (KS / NP)-th (NP = 1 at decode sizes; 2 or 4 where more rows per
+// workgroup pay), each in accumulators of its own, so the KS / NP waves of a tile,
+// which sit in one workgroup, compute the same partials for every NP.
 // v_mfma_f32_16x16x32_f16 takes
 //   A = x          16 tokens x 32 k   (lane (t, g): token t = lane & 15, k-slots 8g..8g+7)
 //   B = W^T        32 k x 16 rows     (lane (j, g): row j = lane & 15, the same k-slots)
@@ -518,42 +521,63 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
 // ---------------------------------------------------------------------------
 // Staging of x chunk [cb0, cb1) into LDS by the whole workgroup (8*n*cl
 // half-groups; blockDim is even, so the two halves of a group share a wave).
+// `issue` runs between the last pass's x loads and their LDS writes, so loads it
+// issues (the first weight superblocks) are in flight while that x arrives; the
+// in-order load counter lets the writes wait for x alone.
+template <int T, class F>
+__device__ __forceinline__ void x_stage_then(const MmaArgs &A, uint4 *xu, int cb0, int cb1, F &&issue) {
+    const int halves = 8 * A.n * (cb1 - cb0);   // > 0
+    const int bd = (int)blockDim.x;
+    const int w64 = 64 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    int q0 = 0;
+    for (; q0 + bd < halves; q0 += bd) {   // full passes (uniform trip count)
+        const int q = q0 + (int)threadIdx.x;
+        XHalf X;
+        xhalf_fetch<T>(A, q, cb0, 1, X);
+        xhalf_commit<T>(q, true, X, xu);
+    }
+    const bool has = q0 + w64 < halves;   // scalar: the wave has half-groups in the last pass
+    const int q = q0 + (int)threadIdx.x;
+    XHalf X;
+    if (has) xhalf_fetch<T>(A, q < halves ? q : halves - 1, cb0, 1, X);
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
+    if (has) xhalf_commit<T>(q, q < halves, X, xu);
+}
 template <int T>
 __device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, int cb1) {
-    const int halves = 8 * A.n * (cb1 - cb0);
-    const int w64 = 64 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    for (int q0 = 0; q0 < halves; q0 += (int)blockDim.x) {   // uniform trip count
-        if (q0 + w64 < halves) {                              // scalar: the wave has half-groups
-            const int q = q0 + (int)threadIdx.x;
-            XHalf X;
-            xhalf_fetch<T>(A, q < halves ? q : halves - 1, cb0, 1, X);
-            xhalf_commit<T>(q, q < halves, X, xu);
-        }
-    }
+    x_stage_then<T>(A, xu, cb0, cb1, [] {});
 }
 
 // The body for one weight type.  The wave serves NT row tiles (`wr[i]`/`sr[i]` = its
-// lane's row in tile i and the NVFP4 scales of that row) and its superblocks
-// b = kp + i*KS, i = 0 .. cnt-1, in increasing order (kp and KS are wave-uniform
-// scalars).
+// lane's row in tile i and that row's scales) and phases kw, kw + KW, ..., kw + (NP-1)KW
+// (KW = KS / NP): its superblocks, in increasing order, are
+//     b(i) = kw + i*KW,   i = 0 .. cnt-1,
+// superblock i being of phase kw + (i % NP)*KW and adding into acc[i % NP] (kw and KW
+// are wave-uniform scalars).
 //
 // Decode path: when every wave's superblocks fit one round of loads and their x
 // fits one staging half-group per lane, each wave stages its own x (see below).  Otherwise a ring of kDepth superblocks
 // refills behind the computation, and x is staged in chunks of A.kc superblocks in
 // turn; every wave steps through every chunk (two barriers per step), whether or
 // not it has superblocks there, so all waves meet the same barriers.
-template <int T, int NT, int NG>
-__device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool dec, int g, int t,
+template <int T, int NT, int NG, int NP, int D>
+__device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool dec, int g, int t,
                                          const uint8_t *const (&wr)[NT], const uint8_t *const (&sr)[NT], uint4 *lds,
-                                         f4 (&acc)[NT][NG]) {
+                                         f4 (&acc)[NP][NT][NG]) {
     typedef typename MRawOf<T>::type Raw;
-    constexpr int D = NT == 1 ? kDepth : 2;
+    // Ring depth D; unroll U, a multiple of D and of NP, so that ring slots and
+    // accumulator sets are compile-time indices.
+    constexpr int U = D > NP ? D : NP;
+    static_assert(U % D == 0 && U % NP == 0, "ring and phase sets must tile the unroll");
     const int n = A.n, nb = A.nb, kc = A.kc;
     const uint4 *zero = lds;   // kZeroUnits units of zeros
     uint4 *xu = lds + kZeroUnits;
-    const int cnt = kp < nb ? (nb - 1 - kp) / KS + 1 : 0;   // wave-uniform
-    const int maxcnt = (nb + KS - 1) / KS;                    // workgroup-uniform (the cnt of kp = 0)
-    const int lastb = cnt > 0 ? kp + (cnt - 1) * KS : nb - 1;
+    const int cnt = kw < nb ? (nb - 1 - kw) / KW + 1 : 0;   // wave-uniform
+    const int maxcnt = (nb + KW - 1) / KW;                   // workgroup-uniform (the cnt of kw = 0)
+    auto sb = [&](int i) { return kw + i * KW; };
+    const int lastb = cnt > 0 ? sb(cnt - 1) : nb - 1;
     const int nchunks = (nb + kc - 1) / kc;
     const int tid = (int)threadIdx.x;
     (void)nchunks;
@@ -568,7 +592,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool 
         }
     };
 
-    if (dec) {   // the host guarantees maxcnt <= D and 8 * n * maxcnt <= 64 * kMmaDecRounds
+    if (NP == 1 && dec) {   // (NP > 1: never) the host guarantees maxcnt <= D and 8 * n * maxcnt <= 64 * kMmaDecRounds
         // Each wave stages the x of its own superblocks in a region of its own: its x
         // loads go out ahead of its weight loads, the in-order load counter lets it
         // wait for x alone, and no barrier ties it to the other waves (whose loads,
@@ -582,53 +606,52 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool 
         xu += wave * (maxcnt * 4 * n * kUnitsPerTok);
         const int hq = 8 * n * cnt;   // this wave's half-groups (wave-uniform), one per lane and round
         Raw ring[D][NT];
-        if (hq <= 64) {   // scalar: one round, its loads ahead of the weight loads
+        int q0 = 0;
+        for (; q0 + 64 < hq; q0 += 64) {   // full rounds (several tokens)
             XHalf X;
-            if (cnt > 0) xhalf_fetch<T>(A, lane < hq ? lane : hq - 1, kp, KS, X);
+            xhalf_fetch<T>(A, q0 + lane, kw, KW, X);
+            xhalf_commit<T>(q0 + lane, true, X, xu);
+        }
+        {   // the last round, its loads ahead of the first weight loads
+            XHalf X;
+            const int q = q0 + lane;
+            if (cnt > 0) xhalf_fetch<T>(A, q < hq ? q : hq - 1, kw, KW, X);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kp, lastb), g);
-            if (cnt > 0) xhalf_commit<T>(lane, lane < hq, X, xu);   // LDS order within a wave: no barrier
-        } else {          // several rounds (several tokens), all staged before the weight loads
-            for (int q0 = 0; q0 < hq; q0 += 64) {
-                XHalf X;
-                const int q = q0 + lane;
-                xhalf_fetch<T>(A, q < hq ? q : hq - 1, kp, KS, X);
-                xhalf_commit<T>(q, q < hq, X, xu);
-            }
-#pragma unroll
-            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kp, lastb), g);
+            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kw, lastb), g);
+            if (cnt > 0) xhalf_commit<T>(q, q < hq, X, xu);   // LDS order within a wave: no barrier
         }
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             if (u + 1 < D) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(kp + (u + 1) * KS, lastb), g);
+                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(sb(u + 1), lastb), g);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (u < cnt) {   // scalar branch
                 const uint4 *xa[NG];
                 xa_of(u, xa, xu);
-                msb<T, NT, NG>(ring[u], g, xa, acc);
+                msb<T, NT, NG>(ring[u], g, xa, acc[0]);
             }
         }
         return;
     }
 
-    x_stage<T>(A, xu, 0, min(nb, kc));   // ahead of the weight loads, as above
     Raw ring[D][NT];
+    x_stage_then<T>(A, xu, 0, min(nb, kc), [&] {   // the ring's loads go out behind the first x loads
 #pragma unroll
-    for (int u = 0; u < D; ++u)
+        for (int u = 0; u < D; ++u)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(kp + u * KS, lastb), g);
+            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(sb(u), lastb), g);
+    });
     __syncthreads();
     int chunk = 0;
-    for (int i0 = 0; i0 < cnt; i0 += D) {
+    for (int i0 = 0; i0 < cnt; i0 += U) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int it = i0 + u;
             if (it < cnt) {   // scalar branch
-                const int b = kp + it * KS;
+                const int b = sb(it);
                 while (b >= (chunk + 1) * kc) {   // scalar
                     ++chunk;
                     __syncthreads();
@@ -637,11 +660,11 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool 
                 }
                 const uint4 *xa[NG];
                 xa_of(b - chunk * kc, xa, zero);
-                msb<T, NT, NG>(ring[u], g, xa, acc);
+                msb<T, NT, NG>(ring[u % D], g, xa, acc[u % NP]);
             }
-            if (i0 + D < cnt) {   // refill only when the ring has more to serve
+            if (it + D < cnt) {   // refill only with a superblock the wave still serves
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(kp + (it + D) * KS, lastb), g);
+                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], sr[i], min(sb(it + D), lastb), g);
             }
         }
     }
@@ -654,8 +677,8 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool 
     }
 }
 
-// WV waves per workgroup = WV / KS tile groups x KS superblock phases.  A wave
-// serves NT weight tiles of 16 rows that share the x operands:
+// WV waves per workgroup = WV / KW tile groups x KW waves (KW = KS / NP, each wave
+// NP phases).  A wave serves NT weight tiles of 16 rows that share the x operands:
 //   NT = 1: rows 16u .. 16u+15 of the matrix;
 //   NT = 2, S.data2 set (SW, or a same-shape pair): rows 16u .. 16u+15 of the
 //           matrix and of data2 (SW: gate and up; y gets silu(gate) * up);
@@ -664,13 +687,13 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KS, int kp, bool 
 // Single-tile, single-group Q4_K / NVFP4 launches ask for five waves per SIMD (at
 // most 96 VGPRs), so that the 4864 waves of a gate/up pair at KS = 4 are all resident
 // at once; the others take what their ring of loads needs.
-template <int TS, int NG, int NT>
+template <int TS, int NG, int NT, int NP>
 constexpr int mma_min_waves() {
-    return ((TS & ~(TS_Q4 | TS_F4)) == 0 && NG == 1 && NT == 1) ? 5 : 1;
+    return ((TS & ~(TS_Q4 | TS_F4)) == 0 && NG == 1 && NT == 1 && NP == 1) ? 5 : 1;
 }
 
-template <int TS, int NG, int WV, int NT, bool SW>
-__global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT>())) void mma_kernel(MmaArgs A) {
+template <int TS, int NG, int WV, int NT, bool SW, int NP>
+__global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mma_kernel(MmaArgs A) {
     static_assert(NT == 1 || NT == 2, "one or two tiles per wave");
     static_assert(!SW || NT == 2, "SwiGLU serves gate and up tiles");
     extern __shared__ uint4 lds[];
@@ -680,8 +703,11 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT>())) void mma_ke
     const MSeg S = in2 ? A.seg[2] : (in1 ? A.seg[1] : A.seg[0]);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // scalar
-    const int KS = S.ks, lks = __builtin_ctz((unsigned)KS), tpw = WV >> lks;
-    const int kp = wave & (KS - 1), rt = wave >> lks;
+    const int KS = S.ks, KW = KS / NP, lkw = __builtin_ctz((unsigned)KW), tpw = WV >> lkw;
+    const int kw = wave & (KW - 1), rt = wave >> lkw;
+    // Ring depth: three superblocks for one tile and phase, two for two tiles; with
+    // several phases four (two in 16-wave workgroups, which have 128 registers).
+    constexpr int D = NP == 1 ? (NT == 1 ? kDepth : 2) : (NT == 1 && WV <= 8 ? 4 : 2);
     const int j = lane & 15, g = lane >> 4;
     const bool two_mats = NT == 2 && (SW || S.data2 != nullptr);   // segment-uniform
     const int64_t unit = (int64_t)(bid - S.wg_begin) * tpw + rt;
@@ -704,44 +730,64 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT>())) void mma_ke
         sr[i] = S.type == T_NVFP4 ? sc + r * (S.row_bytes / 8)
                                   : (S.type == T_FP8 ? sc + (r >> 7) * (S.row_bytes / 64) : nullptr);
     }
-    f4 acc[NT][NG];
+    f4 ph[NP][NT][NG];   // one set of accumulators per phase of the wave
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
+    for (int a = 0; a < NP; ++a)
 #pragma unroll
-        for (int q = 0; q < NG; ++q) acc[i][q] = (f4){0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int q = 0; q < NG; ++q) ph[a][i][q] = (f4){0.f, 0.f, 0.f, 0.f};
     if ((TS & TS_Q4) && S.type == T_Q4_K)
-        mma_body<T_Q4_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_Q5) && S.type == T_Q5_K)
-        mma_body<T_Q5_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_Q6) && S.type == T_Q6_K)
-        mma_body<T_Q6_K, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_F4) && S.type == T_NVFP4)
-        mma_body<T_NVFP4, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_F8) && S.type == T_FP8)
-        mma_body<T_FP8, NT, NG>(A, KS, kp, S.dec != 0, g, j, wr, sr, lds, acc);
+        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
 
-    // Partials of the KS waves of a row tile, added in wave order.
-    if (KS > 1) {
-        constexpr int per = NT * NG;   // 16-byte partials per lane
-        f4 *part = reinterpret_cast<f4 *>(lds);
-        __syncthreads();
-        if (kp != 0) {
+    // The KS phase partials of a row tile, added in phase order:
+    //     y = (((p0 + p1) + p2) + ...) + p(KS-1).
+    // Phase p is set p / KW of wave p % KW of the tile.  One wave holding them all adds
+    // them in registers; otherwise every wave parks its sets in LDS slots (tile group,
+    // phase) and the tile's first wave adds the KS slots in order.
+    constexpr int per = NT * NG;   // 16-byte partials per lane
+    f4 *part = reinterpret_cast<f4 *>(lds);
+    f4(&acc)[NT][NG] = ph[0];
+    if (KW == 1) {
+#pragma unroll
+        for (int a = 1; a < NP; ++a)
 #pragma unroll
             for (int i = 0; i < NT; ++i)
 #pragma unroll
-                for (int q = 0; q < NG; ++q) part[(wave * per + i * NG + q) * 64 + lane] = acc[i][q];
+                for (int q = 0; q < NG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][q][e] += ph[a][i][q][e];
+    } else {
+        __syncthreads();   // every wave is done reading x from LDS
+#pragma unroll
+        for (int a = 0; a < NP; ++a) {
+            const int slot = rt * KS + kw + a * KW;
+            if (kw != 0 || a != 0) {
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) part[(slot * per + i * NG + q) * 64 + lane] = ph[a][i][q];
+            }
         }
         __syncthreads();
-        if (kp != 0) return;
-        for (int w = 1; w < KS; ++w) {
-            const int src = wave + w;
+        if (kw != 0) return;
+        for (int p = 1; p < KS; ++p) {
+            const int slot = rt * KS + p;
 #pragma unroll
             for (int i = 0; i < NT; ++i)
 #pragma unroll
                 for (int q = 0; q < NG; ++q) {
-                    const f4 p = part[(src * per + i * NG + q) * 64 + lane];
+                    const f4 v = part[(slot * per + i * NG + q) * 64 + lane];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][q][e] += p[e];
+                    for (int e = 0; e < 4; ++e) acc[i][q][e] += v[e];
                 }
         }
     }

@@ -5,45 +5,59 @@
 
 namespace qg {
 
-template <int TS, int NG, int WV, int NT, bool SW>
+template <int TS, int NG, int WV, int NT, bool SW, int NP>
 static hipError_t launch_one(const MmaArgs &A, int grid, size_t lds, hipStream_t st) {
-    const void *fn = (const void *)mma_kernel<TS, NG, WV, NT, SW>;
+    const void *fn = (const void *)mma_kernel<TS, NG, WV, NT, SW, NP>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((mma_kernel<TS, NG, WV, NT, SW>), dim3(grid), dim3(64 * WV), lds, st, A);
+    hipLaunchKernelGGL((mma_kernel<TS, NG, WV, NT, SW, NP>), dim3(grid), dim3(64 * WV), lds, st, A);
     return hipGetLastError();
 }
 
-template <int NG, int WV, int NT, bool SW>
+template <int NG, int WV, int NT, bool SW, int NP>
 static hipError_t launch_ts(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
     switch (ts) {
-    case TS_Q4: return launch_one<TS_Q4, NG, WV, NT, SW>(A, grid, lds, st);
-    case TS_Q5: return launch_one<TS_Q5, NG, WV, NT, SW>(A, grid, lds, st);
-    case TS_Q6: return launch_one<TS_Q6, NG, WV, NT, SW>(A, grid, lds, st);
-    case TS_F4: return launch_one<TS_F4, NG, WV, NT, SW>(A, grid, lds, st);
-    case TS_F8: return launch_one<TS_F8, NG, WV, NT, SW>(A, grid, lds, st);
+    case TS_Q4: return launch_one<TS_Q4, NG, WV, NT, SW, NP>(A, grid, lds, st);
+    case TS_Q5: return launch_one<TS_Q5, NG, WV, NT, SW, NP>(A, grid, lds, st);
+    case TS_Q6: return launch_one<TS_Q6, NG, WV, NT, SW, NP>(A, grid, lds, st);
+    case TS_F4: return launch_one<TS_F4, NG, WV, NT, SW, NP>(A, grid, lds, st);
+    case TS_F8: return launch_one<TS_F8, NG, WV, NT, SW, NP>(A, grid, lds, st);
     default:
-        if constexpr (SW) return hipErrorInvalidValue;   // SwiGLU pairs share one type
-        else if (ts == (TS_Q4 | TS_Q6)) return launch_one<TS_Q4 | TS_Q6, NG, WV, NT, false>(A, grid, lds, st);
-        else return launch_one<TS_ALL, NG, WV, NT, false>(A, grid, lds, st);
+        // SwiGLU pairs share one type; several phases per wave take one type per launch.
+        if constexpr (SW || NP > 1) return hipErrorInvalidValue;
+        else if (ts == (TS_Q4 | TS_Q6)) return launch_one<TS_Q4 | TS_Q6, NG, WV, NT, false, 1>(A, grid, lds, st);
+        else return launch_one<TS_ALL, NG, WV, NT, false, 1>(A, grid, lds, st);
     }
 }
 
-template <int NG, int WV>
+template <int NG, int WV, int NP>
 static hipError_t launch_nt(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
-    if (A.mode == MODE_SWIGLU) return launch_ts<NG, WV, 2, true>(A, ts, grid, lds, st);
-    if (A.nt == 2) {
-        if constexpr (WV <= 8) return launch_ts<NG, WV, 2, false>(A, ts, grid, lds, st);
+    if (A.mode == MODE_SWIGLU) {
+        if constexpr (NP == 1 || (NP == 2 && WV <= 8)) return launch_ts<NG, WV, 2, true, NP>(A, ts, grid, lds, st);
         else return hipErrorInvalidValue;
     }
-    return launch_ts<NG, WV, 1, false>(A, ts, grid, lds, st);
+    if (A.nt == 2) {
+        if constexpr (WV <= 8 && NP <= 2) return launch_ts<NG, WV, 2, false, NP>(A, ts, grid, lds, st);
+        else return hipErrorInvalidValue;
+    }
+    return launch_ts<NG, WV, 1, false, NP>(A, ts, grid, lds, st);
+}
+
+template <int WV, int NP>
+static hipError_t launch_np(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
+    return A.n > 16 ? launch_nt<2, WV, NP>(A, ts, grid, lds, st) : launch_nt<1, WV, NP>(A, ts, grid, lds, st);
 }
 
 template <int WV>
 static hipError_t launch_wv(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
-    return A.n > 16 ? launch_nt<2, WV>(A, ts, grid, lds, st) : launch_nt<1, WV>(A, ts, grid, lds, st);
+    if (A.np == 1) return launch_np<WV, 1>(A, ts, grid, lds, st);
+    if constexpr (WV >= 8) {
+        if (A.np == 2) return launch_np<WV, 2>(A, ts, grid, lds, st);
+        if (A.np == 4) return launch_np<WV, 4>(A, ts, grid, lds, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qg

@@ -14,19 +14,21 @@ constexpr int kMmaDecRounds = 4;
 
 struct MSeg {
     const uint8_t *data;     // superblocks, or NVFP4 codes
-    const uint8_t *scales;   // NVFP4 e4m3 scales, else null
+    const uint8_t *scales;   // NVFP4 e4m3 scales or FP8 bf16 block scales, else null
     float *y;                // [n][m]
     const float *resid;      // [n][m] or null
     const uint8_t *data2;    // second matrix served by the same waves (same shape and type):
                              // SwiGLU's up matrix, or the second matrix of a pair; else null
-    const uint8_t *scales2;  // its NVFP4 scales
+    const uint8_t *scales2;  // its scales
     float *y2;               // the pair's second output (unused for SwiGLU)
-    int64_t row_bytes;       // bytes per stored row (NVFP4: codes)
+    int64_t row_bytes;       // bytes per stored row (NVFP4, FP8: codes)
     int32_t type;
     int32_t m;
-    int32_t ks;              // waves splitting K per row tile (1, 2, 4, 8 or 16; divides wv)
+    int32_t ks;              // K phases per row tile (1, 2, 4, 8 or 16): phase p sums superblocks
+                             // p, p + ks, ...; the phases' partials are added in phase order.
+                             // A function of (type, m, k) only.
     int32_t wg_begin;        // first workgroup of this matrix
-    int32_t dec;             // 1: every wave stages its own x (decode path; needs
+    int32_t dec;             // 1: every wave stages its own x (decode path, np = 1; needs
                              //    ceil(nb/ks) <= kMmaDepth (2 with two tiles per wave),
                              //    8*n*ceil(nb/ks) <= 64*kMmaDecRounds, and LDS for
                              //    wv*ceil(nb/ks)*n*576 bytes after the 144 of zeros)
@@ -41,14 +43,19 @@ struct MmaArgs {
     int32_t nb;              // k / 256
     int32_t n;               // tokens, 1..32
     int32_t kc;              // superblocks per staged x chunk
-    int32_t wv;              // waves per workgroup (4, 8 or 16)
+    int32_t wv;              // waves per workgroup (4, 8 or 16; 8 or 16 when np > 1)
     int32_t nt;              // weight tiles per wave (1 or 2; 2 for SwiGLU)
     int32_t mode;            // MODE_PLAIN or MODE_SWIGLU
+    int32_t np;              // phases per wave (1, 2 or 4; divides every segment's ks): a row
+                             // tile has kw = ks / np waves, wave w holding phases w, w + kw, ...
+    int32_t pad;
 };
 
 // ts: bit set of the weight types in the launch (TS_Q4 | ...); grid: workgroups of
 // 64 * A.wv threads; lds: dynamic LDS bytes.  Two tiles per wave (A.nt = 2) are
-// instantiated for workgroups of 4 and 8 waves.
+// instantiated for workgroups of 4 and 8 waves (and SwiGLU for 16 at np = 1); np > 1
+// for one weight type per launch and workgroups of 8 or 16 waves (two tiles per wave:
+// np = 2 and 8 waves).
 hipError_t launch_mma(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
 hipError_t launch_mma_w4(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
 hipError_t launch_mma_w8(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);

@@ -175,8 +175,9 @@ def test_repeat_calls_are_bit_identical():
 
 
 # 3 tokens: the decode path; 20 and 32: the general path (gate and up tiles in one
-# wave, x staged per workgroup in 160 KB chunks).
-@pytest.mark.parametrize("m,n", [(384, 3), (384, 20), (3000, 32)])
+# wave, x staged per workgroup in 160 KB chunks); 9728 rows at 32 tokens: two K
+# phases per wave.
+@pytest.mark.parametrize("m,n", [(384, 3), (384, 20), (3000, 32), (9728, 32)])
 def test_swiglu_pair(m, n):
     import torch
     k = 2560
@@ -208,3 +209,28 @@ def test_q6k_full_int8_scale_range():
         torch.cuda.synchronize()
         y_ref, a = oracle.gemm(qg.Q6_K, data, None, m, k, x)
         assert_within(y.cpu().numpy(), y_ref, a, what="q6k full scales")
+
+
+# Several K phases per wave.  8190 x 7936 has 512 row tiles (the last ragged) and 31
+# superblocks in 16 phases (the last period 15 long): below 4 tokens a wave computes
+# two phases, from 4 tokens on four; every row must keep the bits of its one-token
+# call, and the sums stay within the tolerance of the oracle's.
+@pytest.mark.parametrize("wt", [qg.Q4_K, qg.Q6_K, qg.FP8])
+def test_phases_per_wave_keep_rows_bit_identical(wt):
+    import torch
+    m, k = 8190, 7936
+    print(f"phases type={wt} {m}x{k} N=1..32", flush=True)
+    w, data, scales = weight(wt, m, k, 301)
+    x = synth.duplicate_rows(synth.activations(32, k, synth.rng_for(302)))
+    xd = x_dev(x)
+    singles = [bits(qg.qgemv(w, xd[t])) for t in range(32)]
+    for n in (2, 3, 4, 5, 16, 17, 32):
+        yb = bits(qg.qgemm_rows(w, xd[:n]))
+        for t in range(n):
+            assert np.array_equal(yb[t], singles[t]), f"type {wt}: n={n} row {t} differs from n=1"
+    y = qg.qgemm_rows(w, xd)
+    torch.cuda.synchronize()
+    rng = synth.rng_for(303, wt)
+    rows = np.unique(np.concatenate([[0, 1, m - 2, m - 1], rng.choice(m, size=96, replace=False)]))
+    y_ref, a = oracle.gemm(wt, data, scales, m, k, x, rows=rows)
+    assert_within(y.cpu().numpy()[:, rows], y_ref, a, what=f"phases type {wt}")
