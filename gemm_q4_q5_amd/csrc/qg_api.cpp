@@ -114,10 +114,10 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     memset(&a, 0, sizeof a);
     const int64_t k = w[0]->k;
     const bool sw = mode == qg::MODE_SWIGLU;
-    // Two matrices of one shape and type (SwiGLU, or a gate/up pair above 16
-    // tokens) are served by the same waves, one tile of each per wave, sharing the
-    // x operands.
-    const bool fuse2 = sw || (n > 16 && nseg == 2 && w[0]->type == w[1]->type && w[0]->m == w[1]->m);
+    // SwiGLU's gate and up tiles are served by the same waves (one tile of each per
+    // wave, sharing the x operands), since one lane forms silu(g) * u.  Other calls
+    // give each matrix its own segment (one tile per wave).
+    const bool fuse2 = sw;
     a.x = x;
     a.nseg = fuse2 ? 1 : nseg;
     a.k = (int32_t)k;
@@ -125,18 +125,13 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     a.n = n;
     a.mode = mode;
     a.nt = fuse2 ? 2 : 1;
-    // K phases of each matrix (fixed by its shape: the arithmetic of every row);
-    // every matrix's, also the second of a pair served by the same waves.
+    // K phases of each matrix (fixed by its shape: the arithmetic of every row).
     int ks[3] = {1, 1, 1};
     int ksmax = 1, ksmin = 16;
     for (int s = 0; s < nseg; ++s) {
         ks[s] = choose_ks(w[s]->type, w[s]->m, k);
         ksmax = std::max(ksmax, ks[s]);
         ksmin = std::min(ksmin, ks[s]);
-    }
-    if (!sw && a.nt == 2 && ksmax > 8) {   // a plain pair takes two tiles per wave only up to 8 waves
-        a.nt = 1;
-        a.nseg = 2;
     }
     const int ng = n > 16 ? 2 : 1;
     const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
@@ -148,29 +143,93 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
         return maxcnt <= depth && 8 * n * maxcnt <= 64 * qg::kMmaDecRounds && need <= kMmaLdsBudget;
     };
-    bool any_dec = false;
-    for (int s = 0; s < a.nseg; ++s) any_dec = any_dec || dec_ok(s, std::max(4, ksmax));
-    // Phases per wave (np).  Only the number of waves serving a tile changes with it,
-    // never a row's arithmetic, so it may follow n.  A wave with np phases streams
-    // np times the superblocks and a workgroup serves np times the rows, which
-    // shares each staged chunk of x among more rows.  Taken where the launch keeps
-    // enough waves: at least 4096 (16 per CU) below 8 tokens, where the decode path
-    // (np = 1) stays whenever its workgroups are at most 8 waves; at least 1216 from
-    // 8 tokens on.  Measured on cold rotations (us per call, np 1 -> chosen):
-    // 16384x8192 FP8 at 1 / 32 tokens 38 -> 28 / 129 -> 46; the 151936x2560 Q4_K
-    // head at 8 / 32 tokens 100 -> 61 / 138 -> 86; 9728x2560 Q4_K at 32 tokens 19.5 -> 13.5.
-    int64_t waves1 = 0;   // waves at one phase per wave
-    for (int s = 0; s < a.nseg; ++s) waves1 += (w[s]->m + 15) / 16 * ks[s];
     bool one_type = true;
     for (int s = 1; s < nseg; ++s) one_type = one_type && w[s]->type == w[0]->type;
-    int np = 1;
-    if (one_type && !(n < 8 && any_dec && ksmax <= 8)) {
-        const int64_t want = n < 8 ? 4096 : 1216;
-        for (int p = a.nt == 2 ? 2 : 4; p >= 2; p /= 2)
-            if (ksmin >= p && waves1 / p >= want) {
+    // Several phases per wave take one weight type per launch; two tiles per wave at
+    // most two phases (register budget).
+    const int np_max = !one_type ? 1 : (a.nt == 2 ? 2 : 4);
+    // Rows per workgroup: 16 * wv / (ks / np) for each matrix.
+    auto grid_for = [&](int wv, int np) {
+        int gr = 0;
+        for (int s = 0; s < a.nseg; ++s) {
+            const int64_t rows_per_wg = 16 * (wv / (ks[s] / np));
+            gr += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
+        }
+        return gr;
+    };
+    // Phases per wave (np) and waves per workgroup (wv).  Only the number of waves
+    // serving a tile changes with np, never a row's arithmetic, so both may follow n.
+    // A wave with np phases streams np times the superblocks and a workgroup serves
+    // np times the rows, which shares each staged chunk of x among more rows.
+    constexpr int kCUs = 256;
+    constexpr int kOneRound = 320;
+    int np = 1, wv = 0;
+    bool any_dec = false;
+    for (int s = 0; s < a.nseg; ++s) any_dec = any_dec || dec_ok(s, std::max(4, ksmax));
+    if (n < 8) {
+        // Below 8 tokens the decode path (np = 1) stays whenever its workgroups are at
+        // most 8 waves; otherwise np = 2 or 4 where at least 4096 waves (16 per CU)
+        // remain: 16384x8192 FP8 / NVFP4 at one token 38.6 -> 29.8 / 27.1 -> 18.9 us.
+        if (!(any_dec && ksmax <= 8)) {
+            int64_t waves1 = 0;   // waves at one phase per wave
+            for (int s = 0; s < a.nseg; ++s) waves1 += (w[s]->m + 15) / 16 * ks[s];
+            for (int p = np_max; p >= 2; p /= 2)
+                if (ksmin >= p && waves1 / p >= 4096) {
+                    np = p;
+                    break;
+                }
+        }
+        if (np > 1) any_dec = false;
+        // The general path takes at least eight waves per workgroup and doubles them
+        // while that brings the grid to about one workgroup per CU, which then may take
+        // all of the CU's LDS for fewer, larger x chunks.
+        wv = std::max(4, ksmax / np);
+        if (!any_dec) {
+            const int wv_max = a.nt == 2 ? 8 : 16;
+            wv = std::max(wv, 8);
+            for (int cand = wv; cand <= wv_max; cand *= 2)
+                if (grid_for(cand, np) <= kOneRound) {
+                    wv = cand;
+                    break;
+                }
+        }
+    } else {
+        // From 8 tokens on x staging sets the pace: the largest grid of at most one
+        // workgroup per CU, preferring (on equal grids) two phases per wave, then
+        // 16-wave workgroups.  Without such a grid (large matrices), the most phases
+        // per wave and 8-wave workgroups.  Measured at 8 / 16 / 32 tokens (cold rotations, us):
+        // the gate/up pair 15.4 -> 13.4 / 15.9 -> 14.4 / 21.0 -> 19.3 (two phases,
+        // 16 waves, 152 workgroups) against the next best choices; the Q6_K down
+        // 2560x9728 keeps 160 workgroups of 8 waves with two phases (26.9 at 32
+        // tokens, 27.9 with 16 waves and one phase), Wo 2560x4096 160 of 8 with one
+        // (11.9; 14.3 with two).
+        static const int kPref[7][2] = {{16, 2}, {8, 2}, {16, 4}, {8, 4}, {16, 1}, {8, 1}, {4, 1}};
+        bool dec4 = true;   // every matrix takes the decode path in 4-wave workgroups
+        for (int s = 0; s < a.nseg; ++s) dec4 = dec4 && dec_ok(s, 4);
+        int best = 0;
+        for (const auto &c : kPref) {
+            const int cw = c[0], p = c[1];
+            if (p > np_max || ksmin < p || ksmax / p > cw || (a.nt == 2 && cw > 8) || (cw == 4 && !dec4)) continue;
+            const int gr = grid_for(cw, p);
+            if (gr <= kCUs && gr > best) {
+                best = gr;
+                wv = cw;
                 np = p;
-                break;
             }
+        }
+        // One phase per wave is all the grid search found: small matrices whose waves
+        // all fit the decode path stay there (the QKV triple at 8 tokens 8.0 us, 9.6 in
+        // 8-wave workgroups on the general path).
+        if (best > 0 && np == 1 && dec4 && ksmax <= 4) wv = 4;
+        if (best == 0) {
+            np = 1;
+            for (int p = np_max; p >= 2; p /= 2)
+                if (ksmin >= p) {
+                    np = p;
+                    break;
+                }
+            wv = std::max(8, ksmax / np);
+        }
     }
     a.np = np;
     int kw[3] = {1, 1, 1};   // waves per row tile
@@ -178,36 +237,6 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     for (int s = 0; s < a.nseg; ++s) {
         kw[s] = ks[s] / np;
         kwmax = std::max(kwmax, kw[s]);
-    }
-    if (np > 1) any_dec = false;
-    const int wv0 = std::max(4, kwmax);   // workgroups of at least four waves
-    auto grid_of = [&](int wv) {
-        int gr = 0;
-        for (int s = 0; s < a.nseg; ++s) {
-            const int64_t rows_per_wg = 16 * (wv / kw[s]);
-            gr += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
-        }
-        return gr;
-    };
-    // The general path stages x per workgroup in chunks of kc superblocks, and each
-    // chunk change costs a round of x loads behind the weight stream.  A grid of about
-    // one workgroup per CU (256 CUs) may take all of the CU's LDS for fewer, larger
-    // chunks, so the general path doubles the workgroup (more row tiles share each
-    // chunk) when that brings the grid down to that size.  At 32 tokens: down 35 -> 27
-    // us and Wo 16 -> 12 (already 160 workgroups), the triple 15 -> 12 and the gate/up
-    // pair 30 -> 27 (eight waves); larger grids keep 64 KB and two workgroups per CU.
-    // The general path takes at least eight waves (two row tiles per chunk of x at
-    // KS = 4): the 151936-row NVFP4 head at 16 / 32 tokens, 147 -> 95 / 207 -> 127 us.
-    constexpr int kOneRound = 320;
-    int wv = wv0;
-    if (!any_dec) {
-        const int wv_max = a.nt == 2 ? 8 : 16;
-        wv = std::max(wv0, 8);
-        for (int cand = wv; cand <= wv_max; cand *= 2)
-            if (grid_of(cand) <= kOneRound) {
-                wv = cand;
-                break;
-            }
     }
     a.wv = wv;
     int grid = 0;
