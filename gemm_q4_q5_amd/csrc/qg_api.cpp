@@ -114,17 +114,17 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     memset(&a, 0, sizeof a);
     const int64_t k = w[0]->k;
     const bool sw = mode == qg::MODE_SWIGLU;
-    // SwiGLU's gate and up tiles are served by the same waves (one tile of each per
-    // wave, sharing the x operands), since one lane forms silu(g) * u.  Other calls
-    // give each matrix its own segment (one tile per wave).
-    const bool fuse2 = sw;
+    // Every matrix is a segment of one-tile waves, except SwiGLU: one segment whose tile
+    // groups come in pairs (gate rows, then the same up rows) in one workgroup, the
+    // gate group handing its sums to the up group, which stores silu(g) * u.
+    const int pair = sw ? 2 : 1;   // tile groups per block of 16 output rows
     a.x = x;
-    a.nseg = fuse2 ? 1 : nseg;
+    a.nseg = sw ? 1 : nseg;
     a.k = (int32_t)k;
     a.nb = (int32_t)(k / 256);
     a.n = n;
     a.mode = mode;
-    a.nt = fuse2 ? 2 : 1;
+    a.nt = 1;
     // K phases of each matrix (fixed by its shape: the arithmetic of every row).
     int ks[3] = {1, 1, 1};
     int ksmax = 1, ksmin = 16;
@@ -137,7 +137,7 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
     // Decode path (each wave stages its own x, one phase per wave) where a wave's
     // superblocks fit one round of loads and their x one staging half-group per lane.
-    const int depth = a.nt == 2 ? 2 : qg::kMmaDepth;
+    const int depth = qg::kMmaDepth;
     auto dec_ok = [&](int s, int wv) {
         const int maxcnt = (a.nb + ks[s] - 1) / ks[s];
         const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
@@ -145,14 +145,15 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     };
     bool one_type = true;
     for (int s = 1; s < nseg; ++s) one_type = one_type && w[s]->type == w[0]->type;
-    // Several phases per wave take one weight type per launch; two tiles per wave at
-    // most two phases (register budget).
-    const int np_max = !one_type ? 1 : (a.nt == 2 ? 2 : 4);
-    // Rows per workgroup: 16 * wv / (ks / np) for each matrix.
+    // Several phases per wave take one weight type per launch.
+    const int np_max = one_type ? 4 : 1;
+    // SwiGLU's paired tile groups need 2 * ks / np <= 16 waves per workgroup.
+    const int np_min = sw ? std::max(1, 2 * ksmax / 16) : 1;
+    // Rows per workgroup: 16 * wv / (ks / np) / pair for each matrix.
     auto grid_for = [&](int wv, int np) {
         int gr = 0;
         for (int s = 0; s < a.nseg; ++s) {
-            const int64_t rows_per_wg = 16 * (wv / (ks[s] / np));
+            const int64_t rows_per_wg = 16 * (wv / (ks[s] / np)) / pair;
             gr += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
         }
         return gr;
@@ -170,22 +171,23 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         // Below 8 tokens the decode path (np = 1) stays whenever its workgroups are at
         // most 8 waves; otherwise np = 2 or 4 where at least 4096 waves (16 per CU)
         // remain: 16384x8192 FP8 / NVFP4 at one token 38.6 -> 29.8 / 27.1 -> 18.9 us.
-        if (!(any_dec && ksmax <= 8)) {
+        if (!(any_dec && pair * ksmax <= 8)) {
             int64_t waves1 = 0;   // waves at one phase per wave
-            for (int s = 0; s < a.nseg; ++s) waves1 += (w[s]->m + 15) / 16 * ks[s];
+            for (int s = 0; s < a.nseg; ++s) waves1 += (w[s]->m + 15) / 16 * ks[s] * pair;
             for (int p = np_max; p >= 2; p /= 2)
                 if (ksmin >= p && waves1 / p >= 4096) {
                     np = p;
                     break;
                 }
         }
+        np = std::max(np, np_min);
         if (np > 1) any_dec = false;
         // The general path takes at least eight waves per workgroup and doubles them
         // while that brings the grid to about one workgroup per CU, which then may take
         // all of the CU's LDS for fewer, larger x chunks.
-        wv = std::max(4, ksmax / np);
+        wv = std::max(sw ? 8 : 4, pair * ksmax / np);
         if (!any_dec) {
-            const int wv_max = a.nt == 2 ? 8 : 16;
+            const int wv_max = 16;
             wv = std::max(wv, 8);
             for (int cand = wv; cand <= wv_max; cand *= 2)
                 if (grid_for(cand, np) <= kOneRound) {
@@ -209,7 +211,8 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         int best = 0;
         for (const auto &c : kPref) {
             const int cw = c[0], p = c[1];
-            if (p > np_max || ksmin < p || ksmax / p > cw || (a.nt == 2 && cw > 8) || (cw == 4 && !dec4)) continue;
+            if (p > np_max || p < np_min || ksmin < p || pair * ksmax / p > cw || (sw && cw < 8) || (cw == 4 && !dec4))
+                continue;
             const int gr = grid_for(cw, p);
             if (gr <= kCUs && gr > best) {
                 best = gr;
@@ -220,7 +223,7 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         // One phase per wave is all the grid search found: small matrices whose waves
         // all fit the decode path stay there (the QKV triple at 8 tokens 8.0 us, 9.6 in
         // 8-wave workgroups on the general path).
-        if (best > 0 && np == 1 && dec4 && ksmax <= 4) wv = 4;
+        if (best > 0 && np == 1 && dec4 && pair * ksmax <= 4) wv = 4;
         if (best == 0) {
             np = 1;
             for (int p = np_max; p >= 2; p /= 2)
@@ -228,7 +231,8 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
                     np = p;
                     break;
                 }
-            wv = std::max(8, ksmax / np);
+            np = std::max(np, np_min);
+            wv = std::max(8, pair * ksmax / np);
         }
     }
     a.np = np;
@@ -251,16 +255,17 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         g.m = (int32_t)w[s]->m;
         g.ks = ks[s];
         g.wg_begin = grid;
-        if (a.nt == 2) {
+        if (sw) {
             g.data2 = (const uint8_t *)w[1]->data;
             g.scales2 = (const uint8_t *)w[1]->scales;
-            g.y2 = sw ? nullptr : y[1];
         }
-        const int64_t rows_per_wg = 16 * (wv / kw[s]);
+        const int64_t rows_per_wg = 16 * (wv / kw[s]) / pair;
         grid += (int)((w[s]->m + rows_per_wg - 1) / rows_per_wg);
     }
     const size_t budget = grid <= kOneRound ? kMmaLdsMax : kMmaLdsBudget;
-    const int kc = (int)std::max<size_t>(1, (budget - kMmaZeroBytes) / per_sb);
+    // SwiGLU: the hand-over region (a slot per tile-group pair) comes out of the budget.
+    const size_t xch_bytes = sw ? (size_t)(wv / kwmax / 2) * ng * 1024 : 0;
+    const int kc = (int)std::max<size_t>(1, (budget - kMmaZeroBytes - xch_bytes) / per_sb);
     a.kc = std::min(kc, a.nb);
     size_t lds = kMmaZeroBytes;
     for (int s = 0; s < a.nseg; ++s) {
@@ -273,7 +278,12 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     }
     // Partial sums of the K phases: a slot per phase and tile group, where a tile has
     // more than one wave.
-    if (kwmax > 1) lds = std::max(lds, (size_t)wv * np * 1024 * ng * a.nt);
+    if (kwmax > 1) lds = std::max(lds, (size_t)wv * np * 1024 * ng);
+    if (sw) {   // where the gate groups hand over their sums: after everything else
+        lds = (lds + 15) / 16 * 16;
+        a.xch = (int32_t)(lds / 16);
+        lds += xch_bytes;
+    }
     int ts = 0;
     for (int s = 0; s < nseg; ++s) ts |= qg::type_bit(w[s]->type);
     hipError_t e = qg::launch_mma(a, ts, grid, lds, (hipStream_t)stream);

@@ -678,12 +678,11 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool 
 }
 
 // WV waves per workgroup = WV / KW tile groups x KW waves (KW = KS / NP, each wave
-// NP phases).  A wave serves NT weight tiles of 16 rows that share the x operands:
-//   NT = 1: rows 16u .. 16u+15 of the matrix;
-//   NT = 2, S.data2 set (SW, or a same-shape pair): rows 16u .. 16u+15 of the
-//           matrix and of data2 (SW: gate and up; y gets silu(gate) * up);
-//   NT = 2, S.data2 null: rows 32u .. 32u+15 and 32u+16 .. 32u+31 of the matrix.
-// Which wave serves a row never changes the row's instructions.
+// NP phases).  A tile group serves rows 16u .. 16u+15 of the matrix.  SwiGLU (SW):
+// tile groups come in pairs, the gate rows 16u .. 16u+15 and the same rows of the up
+// matrix (S.data2); the gate group hands its sums to the up group through LDS, which
+// stores silu(gate) * up.  Which wave serves a row never changes the row's
+// instructions.
 // Single-tile, single-group Q4_K / NVFP4 launches ask for five waves per SIMD (at
 // most 96 VGPRs), so that the 4864 waves of a gate/up pair at KS = 4 are all resident
 // at once; the others take what their ring of loads needs.
@@ -694,8 +693,7 @@ constexpr int mma_min_waves() {
 
 template <int TS, int NG, int WV, int NT, bool SW, int NP>
 __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mma_kernel(MmaArgs A) {
-    static_assert(NT == 1 || NT == 2, "one or two tiles per wave");
-    static_assert(!SW || NT == 2, "SwiGLU serves gate and up tiles");
+    static_assert(NT == 1, "one weight tile per wave");
     extern __shared__ uint4 lds[];
     const int bid = (int)blockIdx.x;
     const bool in1 = A.nseg > 1 && bid >= A.seg[1].wg_begin;
@@ -705,15 +703,15 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // scalar
     const int KS = S.ks, KW = KS / NP, lkw = __builtin_ctz((unsigned)KW), tpw = WV >> lkw;
     const int kw = wave & (KW - 1), rt = wave >> lkw;
-    // Ring depth: three superblocks for one tile and phase, two for two tiles; with
-    // several phases four (two in 16-wave workgroups, which have 128 registers).
-    constexpr int D = NP == 1 ? (NT == 1 ? kDepth : 2) : (NT == 1 && WV <= 8 ? 4 : 2);
+    // Ring depth: three superblocks with one phase per wave; with several, four (two
+    // in 16-wave workgroups, which have 128 registers).
+    constexpr int D = NP == 1 ? kDepth : (WV <= 8 ? 4 : 2);
     const int j = lane & 15, g = lane >> 4;
-    const bool two_mats = NT == 2 && (SW || S.data2 != nullptr);   // segment-uniform
-    const int64_t unit = (int64_t)(bid - S.wg_begin) * tpw + rt;
+    const int up = SW ? (rt & 1) : 0;   // SwiGLU: 0 for a gate tile group, 1 for an up one
+    const int64_t unit = SW ? (int64_t)(bid - S.wg_begin) * (tpw >> 1) + (rt >> 1)
+                            : (int64_t)(bid - S.wg_begin) * tpw + rt;
     int64_t rows[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) rows[i] = (NT == 2 && !two_mats) ? unit * 32 + 16 * i + j : unit * 16 + j;
+    rows[0] = unit * 16 + j;
     const int n = A.n;
     if (threadIdx.x < kZeroUnits) lds[threadIdx.x] = make_uint4(0, 0, 0, 0);
 
@@ -722,7 +720,7 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t r = rows[i] < S.m ? rows[i] : S.m - 1;   // rows past m read row m-1; results dropped
-        const bool second = two_mats && i == 1;
+        const bool second = up != 0;
         wr[i] = (second ? S.data2 : S.data) + r * S.row_bytes;
         const uint8_t *sc = second ? S.scales2 : S.scales;
         // NVFP4: one e4m3 scale per 16 weights of the row; FP8: the bf16 scale row
@@ -792,25 +790,35 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
         }
     }
     if (SW) {
+        // The waves left hold their tile group's sums (one per group).  LDS from A.xch
+        // on is used by nothing else, so the gate sums go there at once.
+        f4 *xch = reinterpret_cast<f4 *>(lds + A.xch) + (rt >> 1) * NG * 64 + lane;
+        if (!up) {
+#pragma unroll
+            for (int q = 0; q < NG; ++q) xch[q * 64] = acc[0][q];
+        }
+        __syncthreads();   // every surviving wave (the first of each tile group) gets here once
+        if (!up) return;
         if (rows[0] < S.m) {
 #pragma unroll
-            for (int q = 0; q < NG; ++q)
+            for (int q = 0; q < NG; ++q) {
+                const f4 gs = xch[q * 64];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int tok = 16 * q + 4 * g + e;
                     if (tok < n) {
-                        const float gv = acc[0][q][e];
-                        S.y[(int64_t)tok * S.m + rows[0]] = gv / (1.0f + __expf(-gv)) * acc[NT - 1][q][e];
+                        const float gv = gs[e];
+                        S.y[(int64_t)tok * S.m + rows[0]] = gv / (1.0f + __expf(-gv)) * acc[0][q][e];
                     }
                 }
+            }
         }
         return;
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const bool second = two_mats && i == 1;
-        float *y = second ? S.y2 : S.y;
-        const float *resid = second ? nullptr : S.resid;
+        float *y = S.y;
+        const float *resid = S.resid;
         if (rows[i] < S.m) {
 #pragma unroll
             for (int q = 0; q < NG; ++q)

@@ -34,12 +34,9 @@ static hipError_t launch_ts(const MmaArgs &A, int ts, int grid, size_t lds, hipS
 
 template <int NG, int WV, int NP>
 static hipError_t launch_nt(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st) {
-    if (A.mode == MODE_SWIGLU) {
-        if constexpr (NP == 1 || (NP == 2 && WV <= 8)) return launch_ts<NG, WV, 2, true, NP>(A, ts, grid, lds, st);
-        else return hipErrorInvalidValue;
-    }
-    if (A.nt == 2) {
-        if constexpr (WV <= 8 && NP <= 2) return launch_ts<NG, WV, 2, false, NP>(A, ts, grid, lds, st);
+    if (A.nt != 1) return hipErrorInvalidValue;
+    if (A.mode == MODE_SWIGLU) {   // gate and up tile groups in pairs
+        if constexpr (WV >= 8) return launch_ts<NG, WV, 1, true, NP>(A, ts, grid, lds, st);
         else return hipErrorInvalidValue;
     }
     return launch_ts<NG, WV, 1, false, NP>(A, ts, grid, lds, st);

@@ -17,10 +17,9 @@ struct MSeg {
     const uint8_t *scales;   // NVFP4 e4m3 scales or FP8 bf16 block scales, else null
     float *y;                // [n][m]
     const float *resid;      // [n][m] or null
-    const uint8_t *data2;    // second matrix served by the same waves (same shape and type):
-                             // SwiGLU's up matrix, or the second matrix of a pair; else null
+    const uint8_t *data2;    // SwiGLU's up matrix (same shape and type as the gate); else null
     const uint8_t *scales2;  // its scales
-    float *y2;               // the pair's second output (unused for SwiGLU)
+    float *y2;               // unused
     int64_t row_bytes;       // bytes per stored row (NVFP4, FP8: codes)
     int32_t type;
     int32_t m;
@@ -43,19 +42,17 @@ struct MmaArgs {
     int32_t nb;              // k / 256
     int32_t n;               // tokens, 1..32
     int32_t kc;              // superblocks per staged x chunk
-    int32_t wv;              // waves per workgroup (4, 8 or 16; 8 or 16 when np > 1)
-    int32_t nt;              // weight tiles per wave (1 or 2; 2 for SwiGLU)
+    int32_t wv;              // waves per workgroup (4, 8 or 16; 8 or 16 when np > 1 or for SwiGLU)
+    int32_t nt;              // weight tiles per wave (1)
     int32_t mode;            // MODE_PLAIN or MODE_SWIGLU
     int32_t np;              // phases per wave (1, 2 or 4; divides every segment's ks): a row
                              // tile has kw = ks / np waves, wave w holding phases w, w + kw, ...
-    int32_t pad;
+    int32_t xch;             // SwiGLU: 16-byte LDS unit where the gate sums are handed over
 };
 
 // ts: bit set of the weight types in the launch (TS_Q4 | ...); grid: workgroups of
-// 64 * A.wv threads; lds: dynamic LDS bytes.  Two tiles per wave (A.nt = 2) are
-// instantiated for workgroups of 4 and 8 waves (and SwiGLU for 16 at np = 1); np > 1
-// for one weight type per launch and workgroups of 8 or 16 waves (two tiles per wave:
-// np = 2 and 8 waves).
+// 64 * A.wv threads; lds: dynamic LDS bytes.  np > 1 and SwiGLU take one weight type
+// per launch and workgroups of 8 or 16 waves.
 hipError_t launch_mma(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
 hipError_t launch_mma_w4(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
 hipError_t launch_mma_w8(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);

@@ -174,14 +174,14 @@ def test_repeat_calls_are_bit_identical():
     assert np.array_equal(a, b)
 
 
-# 3 tokens: the decode path; 20 and 32: the general path (gate and up tiles in one
-# wave, x staged per workgroup in 160 KB chunks); 9728 rows at 32 tokens: two K
-# phases per wave.
-@pytest.mark.parametrize("m,n", [(384, 3), (384, 20), (3000, 32), (9728, 32)])
-def test_swiglu_pair(m, n):
+# Gate and up tile groups in pairs, the gate sums handed over in LDS.  3 tokens: the
+# decode path; 20 and 32: the general path (x staged per workgroup); 9728 rows at 32
+# tokens: two K phases per wave; K = 9728 (16 K phases, so at least two per wave).
+@pytest.mark.parametrize("m,n,k", [(384, 3, 2560), (384, 20, 2560), (3000, 32, 2560), (9728, 32, 2560),
+                                   (640, 1, 9728), (640, 5, 9728)])
+def test_swiglu_pair(m, n, k):
     import torch
-    k = 2560
-    print(f"swiglu m={m} n={n}", flush=True)
+    print(f"swiglu m={m} n={n} k={k}", flush=True)
     wg, dg, _ = weight(qg.Q4_K, m, k, 91)
     wu, du, _ = weight(qg.Q4_K, m, k, 92)
     x = synth.activations(n, k, synth.rng_for(93, n))
@@ -195,6 +195,11 @@ def test_swiglu_pair(m, n):
     bound = 2e-3 * (1.1 * ag * np.abs(ur) + np.abs(gr) * au) + 1e-6 * np.abs(h_ref)
     err = np.abs(h.cpu().numpy() - h_ref)
     assert (err <= bound).all(), err.max()
+    # row invariance: a row of the n-token call equals its one-token call bit for bit
+    xd = x_dev(x)
+    hb = bits(h)
+    for t in sorted({0, n // 2, n - 1}):
+        assert np.array_equal(hb[t], bits(qg.qgemv_pair_swiglu(wg, wu, xd[t:t + 1]))[0]), f"row {t}"
 
 
 def test_q6k_full_int8_scale_range():
@@ -234,3 +239,25 @@ def test_phases_per_wave_keep_rows_bit_identical(wt):
     rows = np.unique(np.concatenate([[0, 1, m - 2, m - 1], rng.choice(m, size=96, replace=False)]))
     y_ref, a = oracle.gemm(wt, data, scales, m, k, x, rows=rows)
     assert_within(y.cpu().numpy()[:, rows], y_ref, a, what=f"phases type {wt}")
+
+
+# The gate/up pair at the layer's shape: the launch shape changes with n (decode path
+# below 8 tokens, two phases per wave in 16-wave workgroups from 8 on); each output
+# must equal the plain call on its matrix, and every row its one-token call, bit for bit.
+def test_pair_layer_shape_bits_across_launch_shapes():
+    import torch
+    m, k = 9728, 2560
+    wg, _, _ = weight(qg.Q4_K, m, k, 311)
+    wu, _, _ = weight(qg.Q4_K, m, k, 312)
+    x = x_dev(synth.activations(32, k, synth.rng_for(313)))
+    single_g = [bits(qg.qgemv(wg, x[t])) for t in range(32)]
+    single_u = [bits(qg.qgemv(wu, x[t])) for t in range(32)]
+    for n in (1, 4, 7, 8, 9, 16, 17, 32):
+        print(f"pair {m}x{k} n={n}", flush=True)
+        g, u = qg.qgemv_pair(wg, wu, x[:n])
+        torch.cuda.synchronize()
+        gb, ub = bits(g), bits(u)
+        assert np.array_equal(gb, bits(qg.qgemm_rows(wg, x[:n])))
+        assert np.array_equal(ub, bits(qg.qgemm_rows(wu, x[:n])))
+        for t in range(n):
+            assert np.array_equal(gb[t], single_g[t]) and np.array_equal(ub[t], single_u[t]), f"n={n} row {t}"
