@@ -321,10 +321,56 @@ def cpu_baseline(target_s=10.0):
             oracle.gemm(wt, data, scales, m, k, xs[k])
         reps += 1
         t = time.perf_counter() - t0
-    return {"value": layer_bytes * reps / t / 1e9, "unit": "GB/s", "cores": oracle.last_threads(),
-            "kind": "oracle",
-            "sample": f"the full decode layer (7 projections, N=1) {reps} times, {t:.1f} s; "
-                      f"oracle = plain C dequant + fp64 dot, OpenMP over rows"}
+    res = {"value": layer_bytes * reps / t / 1e9, "unit": "GB/s", "cores": oracle.last_threads(),
+           "kind": "oracle",
+           "sample": f"the full decode layer (7 projections, N=1) {reps} times, {t:.1f} s; "
+                     f"oracle = plain C dequant + fp64 dot, OpenMP over rows"}
+    res["extras"] = cpu_extras(mats, xs)
+    return res
+
+
+def _timed(fn, budget_s):
+    """Median of up to 3 timed runs after one warm-up, stopping once budget_s is spent."""
+    fn()
+    ts = []
+    t_end = time.perf_counter() + budget_s
+    while len(ts) < 3 and (not ts or time.perf_counter() < t_end):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def cpu_extras(mats, xs, budget_s=1.5):
+    """The oracle on the other workloads, each bounded to about budget_s: the layer at
+    N=1 on one thread and at N=32 on every core, the 1024x1024 Q4_K call, the 512-token
+    prefill on a sample of 256 output rows, and NVFP4 16384x8192 at N=1."""
+    import oracle
+    import synth
+    out = {}
+    t1 = _timed(lambda: [oracle.gemm(wt, d, sc, m, k, xs[k], nthreads=1) for wt, d, sc, m, k in mats], budget_s)
+    out["layer_n1_one_thread"] = {"ms": round(1e3 * t1, 2),
+                                  "GB/s": round(sum(layer_call_bytes(1).values()) / t1 / 1e9, 3)}
+    x32 = {k: synth.activations(32, k, synth.rng_for(1, 98, k)) for k in (2560, 4096, 9728)}
+    t32 = _timed(lambda: [oracle.gemm(wt, d, sc, m, k, x32[k]) for wt, d, sc, m, k in mats], budget_s)
+    out["layer_n32"] = {"ms": round(1e3 * t32, 2), "GB/s": round(sum(layer_call_bytes(32).values()) / t32 / 1e9, 3),
+                        "threads": oracle.last_threads()}
+    d0, _ = synth.weights(synth.Q4_K, 1024, 1024, synth.rng_for(0, 0))
+    x0 = synth.activations(1, 1024, synth.rng_for(0, 1))
+    t0 = _timed(lambda: oracle.gemm(synth.Q4_K, d0, None, 1024, 1024, x0), budget_s)
+    out["q4k_1024x1024_n1"] = {"us": round(1e6 * t0, 1)}
+    wt, d, sc, m, k = mats[4]   # the gate matrix, Q4_K 9728x2560
+    xp = synth.activations(512, k, synth.rng_for(3, 10))
+    rows = np.arange(0, m, m // 256)[:256]
+    tp = _timed(lambda: oracle.gemm(wt, d, sc, m, k, xp, rows=rows), budget_s)
+    out["prefill_512_q4k_9728x2560_256_rows"] = {"ms": round(1e3 * tp, 2),
+                                                 "GFLOP/s": round(2 * 512 * len(rows) * k / tp / 1e9, 2)}
+    dn, sn = synth.weights(synth.NVFP4, 16384, 8192, synth.rng_for(4, 0))
+    xn = synth.activations(1, 8192, synth.rng_for(4, 10, 1))
+    tn = _timed(lambda: oracle.gemm(synth.NVFP4, dn, sn, 16384, 8192, xn), budget_s)
+    out["nvfp4_16384x8192_n1"] = {"ms": round(1e3 * tn, 2),
+                                  "GB/s": round(call_bytes(synth.NVFP4, 16384, 8192, 1) / tn / 1e9, 3)}
+    return out
 
 
 CAL_BYTES = 1 << 30   # bytes read (and written) by one calibration copy
@@ -472,7 +518,7 @@ def main():
         res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                            "traffic": load_traffic(sha),
-                           "kernel": "qg::mma_kernel<1, 1, 4, 1, false> (qgemv_pair, Q4_K, one token)",
+                           "kernel": "qg::mma_kernel<1, 1, 4, 1, false, 1> (qgemv_pair, Q4_K, one token)",
                            "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
     if not args.no_ceiling:
         ceil = time_read_ceiling(layers, max(1, r1["graph_replays"] // 2))

@@ -247,12 +247,15 @@ int oracle_gemm(int32_t type, const uint8_t *data, const uint8_t *scales,
 
     int err = 0;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-    g_last_threads = omp_get_max_threads();
+    /* nthreads applies to this call only (0: the OpenMP default). */
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+    g_last_threads = nth;
 #else
+    const int nth = 1;
     g_last_threads = 1;
 #endif
-#pragma omp parallel
+    (void)nth;
+#pragma omp parallel num_threads(nth)
     {
         double *w = (double *)malloc(sizeof(double) * k);
         if (!w) {
