@@ -261,3 +261,28 @@ def test_pair_layer_shape_bits_across_launch_shapes():
         assert np.array_equal(ub, bits(qg.qgemm_rows(wu, x[:n])))
         for t in range(n):
             assert np.array_equal(gb[t], single_g[t]) and np.array_equal(ub[t], single_u[t]), f"n={n} row {t}"
+
+
+# The largest K the boundary accepts (2^20 = 4096 superblocks): 16 phases of 256
+# superblocks, x staged in many chunks; 17 rows (a ragged second tile).
+@pytest.mark.parametrize("wt", [qg.Q4_K, qg.Q6_K, qg.FP8])
+def test_maximum_k(wt):
+    import torch
+    m, k = 17, 1 << 20
+    print(f"max k type={wt}", flush=True)
+    w, data, scales = weight(wt, m, k, 321)
+    x = synth.activations(32, k, synth.rng_for(322))
+    xd = x_dev(x)
+    single = [bits(qg.qgemv(w, xd[t])) for t in (0, 4, 31)]
+    for n in (5, 32):
+        y = qg.qgemm_rows(w, xd[:n])
+        torch.cuda.synchronize()
+        yb = bits(y)
+        for i, t in enumerate((0, 4, 31)):
+            if t < n:
+                assert np.array_equal(yb[t], single[i]), f"n={n} row {t}"
+    y_ref, a = oracle.gemm(wt, data, scales, m, k, x)
+    assert_within(y.cpu().numpy(), y_ref, a, what=f"max k type {wt}")
+    yp = qg.qgemm_prefill(w, xd[:3])
+    torch.cuda.synchronize()
+    assert_within(yp.cpu().numpy(), y_ref[:3], a[:3], what=f"max k prefill type {wt}")
