@@ -7,8 +7,11 @@ One step = one pass of the layer's projection calls over one batch of tokens:
   qgemv_pair    gate, up 9728x2560 Q4_K
   qgemv_q6k / qgemm_rows   down 2560x9728 Q6_K
 Weights are synthetic (seeded, the value distributions of the Q4_K_M workload),
-resident in HBM before timing; 36 distinct copies of the layer (2.3 GB, beyond
-the 256 MB Infinity Cache) rotate so every step streams its weights cold.  The
+resident in HBM before timing, repacked once into 16-row tiles (qg_pack_tiles: the
+same superblocks in another order, the same bits of every product; --layout rows
+keeps the row layout, and the row-layout N=1 layer is timed beside it); 36 distinct
+copies of the layer (2.3 GB, beyond the 256 MB Infinity Cache) rotate so every step
+streams its weights cold.  The
 36-layer sequence is captured once in a HIP graph and replayed, so host launch
 overhead is not part of the measurement.
 
@@ -64,7 +67,10 @@ class Layer:
         self.W = W  # name -> QWeight
 
 
-def build_layers(n_layers, seed=1):
+def build_layers(n_layers, seed=1, layout="tiles"):
+    """n_layers distinct copies of the layer's weights, in the row layout as stored or
+    repacked once into 16-row tiles (qg_pack_tiles: the same superblocks in another
+    order, same bits of every product)."""
     import torch
     import gemm_q4_q5_amd as qg
     import synth
@@ -72,10 +78,12 @@ def build_layers(n_layers, seed=1):
     for i, (name, wt, m, k) in enumerate(synth.QWEN3_4B_LAYER):
         data, scales = synth.weights(wt, m, k, synth.rng_for(seed, i))
         base[name] = qg.QWeight.from_host(wt, data, m, k, scales, device="cuda")
+        if layout == "tiles":
+            base[name] = qg.pack_tiles(base[name])
     layers = [Layer(base)]
     for _ in range(1, n_layers):
         layers.append(Layer({nm: qg.QWeight(w.type, w.data.clone(), w.m, w.k,
-                                            None if w.scales is None else w.scales.clone())
+                                            None if w.scales is None else w.scales.clone(), w.layout)
                              for nm, w in base.items()}))
     torch.cuda.synchronize()
     return layers
@@ -105,9 +113,9 @@ def layer_calls(L, B, n):
         ("add", lambda: qg.qgemv_add(W["wo"], B.x_o, B.resid, B.o)),
         ("pair", lambda: qg.qgemv_pair(W["gate"], W["up"], B.x_h, B.g, B.u)),
     ]
-    if n == 1:
+    if n == 1 and W["down"].layout == qg.LAYOUT_ROWS:
         calls.append(("down", lambda: qg.qgemv_q6k(W["down"], B.x_f[0], B.d[0])))
-    else:
+    else:   # the tiled layout goes through qgemm_rows (one token: the same kernel)
         calls.append(("down", lambda: qg.qgemm_rows(W["down"], B.x_f, B.d)))
     return calls
 
@@ -451,6 +459,9 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 large-shape pass")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-stream ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--layout", choices=("tiles", "rows"), default="tiles",
+                    help="weights in 16-row tiles (qg_pack_tiles) or in the row layout as stored")
+    ap.add_argument("--no-rows", action="store_true", help="skip the row-layout N=1 comparison")
     ap.add_argument("--kernel", choices=KERNELS, default=None,
                     help="profile mode: replay only this call over the 36-layer rotation")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per call in --kernel mode")
@@ -472,7 +483,7 @@ def main():
     qg.lib()   # fails loudly if the HIP library is not built
     torch.cuda.set_device(0)
 
-    layers = build_layers(LAYERS)
+    layers = build_layers(LAYERS, layout=args.layout)
     if args.kernel:
         n = args.tokens
         B = Buffers(n)
@@ -504,7 +515,9 @@ def main():
         "config": {"workload": "Qwen3-4B-shaped decode layer: QKV triple (Q4_K,Q4_K,Q6_K) + "
                                "Wo Q4_K with residual + gate/up Q4_K pair + down Q6_K; K=2560 "
                                "hidden, 36 distinct layers rotated (cold)", "tokens": 1,
-                   "bytes_per_step": step_bytes},
+                   "bytes_per_step": step_bytes,
+                   "weight_layout": "16-row tiles (qg_pack_tiles, same superblocks and bits)"
+                   if args.layout == "tiles" else "rows as stored"},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "tok_s_equiv_projections": round(1000.0 / (LAYERS * ms), 1),
     }
@@ -518,7 +531,8 @@ def main():
         res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                            "traffic": load_traffic(sha),
-                           "kernel": "qg::mma_kernel<1, 1, 4, 1, false, 1> (qgemv_pair, Q4_K, one token)",
+                           "kernel": "qg::mma_kernel<1, 1, 4, 1, false, 1> (qgemv_pair, Q4_K, one token, "
+                                     f"{args.layout} layout)",
                            "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
     if not args.no_ceiling:
         ceil = time_read_ceiling(layers, max(1, r1["graph_replays"] // 2))
@@ -534,6 +548,17 @@ def main():
         if "kernel_us" in r32:
             res["n32"]["kernels"] = {k: {"us": round(v, 3), "GB/s": round(b32[k] / (v * 1e3), 1)}
                                      for k, v in r32["kernel_us"].items()}
+    if args.layout == "tiles" and not args.no_rows:
+        del layers
+        torch.cuda.empty_cache()
+        rows = build_layers(LAYERS, layout="rows")
+        rr = time_layer(rows, 1, args.steps, args.warmup)
+        res["rows_layout_n1"] = {"value": round(step_bytes / (rr["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                 "ms_per_step": round(rr["ms_per_step"], 5)}
+        if "kernel_us" in rr:
+            res["rows_layout_n1"]["kernels"] = {k: round(v, 3) for k, v in rr["kernel_us"].items()}
+        del rows
+        torch.cuda.empty_cache()
     if not args.no_prefill:
         res["prefill_n512"] = time_prefill()
     if not args.no_nvfp4:

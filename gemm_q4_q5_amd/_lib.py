@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemm.so")
 
 Q4_K, Q5_K, Q6_K, NVFP4, FP8 = 12, 13, 14, 1001, 1002
+LAYOUT_ROWS, LAYOUT_TILES = 0, 1
 MAX_ROWS = 32
 STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_SHAPE", -3: "QG_ERR_ROWS",
           -4: "QG_ERR_TYPE", -5: "QG_ERR_ALIGN", -6: "QG_ERR_LAUNCH"}
@@ -28,7 +29,7 @@ class QGError(RuntimeError):
 
 
 class CWeight(ctypes.Structure):
-    _fields_ = [("type", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("type", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("m", ctypes.c_int64), ("k", ctypes.c_int64)]
 
@@ -47,6 +48,8 @@ def lib() -> ctypes.CDLL:
         W = ctypes.POINTER(CWeight)
         sig = {
             "qg_row_bytes": ([i32, i64], i64),
+            "qg_tiles_bytes": ([W], i64),
+            "qg_pack_tiles": ([W, p, p], ctypes.c_int),
             "qg_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "qg_last_error": ([], ctypes.c_char_p),
             "qgemv_q4k": ([p, p, fp, i64, i64, p], ctypes.c_int),
@@ -88,9 +91,10 @@ class QWeight:
     m: int
     k: int
     scales: Optional[object] = None  # NVFP4 e4m3 bytes [m, k/16]; FP8 bf16 [ceil(m/128), k/128]
+    layout: int = 0                    # LAYOUT_ROWS, or LAYOUT_TILES (see pack_tiles)
 
     def c(self) -> CWeight:
-        return CWeight(self.type, 0, self.data.data_ptr(),
+        return CWeight(self.type, self.layout, self.data.data_ptr(),
                        self.scales.data_ptr() if self.scales is not None else None, self.m, self.k)
 
     @classmethod
@@ -99,6 +103,19 @@ class QWeight:
         d = torch.from_numpy(data).to(device)
         s = torch.from_numpy(scales).to(device) if scales is not None else None
         return cls(wtype, d, m, k, s)
+
+
+def pack_tiles(w: QWeight) -> QWeight:
+    """The 16-row tiled copy of a row-layout K-quant weight (same values, same bits of
+    every product); a new device buffer of qg_tiles_bytes bytes."""
+    import torch
+    cw = w.c()
+    nbytes = lib().qg_tiles_bytes(ctypes.byref(cw))
+    if nbytes < 0:
+        _check(int(nbytes))
+    dst = torch.empty((int(nbytes),), dtype=torch.uint8, device=w.data.device)
+    _check(lib().qg_pack_tiles(ctypes.byref(cw), _ptr(dst), _stream()))
+    return QWeight(w.type, dst, w.m, w.k, None, LAYOUT_TILES)
 
 
 def _stream():
@@ -122,18 +139,21 @@ def _rows(x) -> int:
 
 
 def qgemv_q4k(w: QWeight, x, y=None):
+    _row_layout(w)
     y = _out((w.m,), x, y)
     _check(lib().qgemv_q4k(_ptr(w.data), _ptr(x), _ptr(y), w.m, w.k, _stream()))
     return y
 
 
 def qgemv_q5k(w: QWeight, x, y=None):
+    _row_layout(w)
     y = _out((w.m,), x, y)
     _check(lib().qgemv_q5k(_ptr(w.data), _ptr(x), _ptr(y), w.m, w.k, _stream()))
     return y
 
 
 def qgemv_q6k(w: QWeight, x, y=None):
+    _row_layout(w)
     y = _out((w.m,), x, y)
     _check(lib().qgemv_q6k(_ptr(w.data), _ptr(x), _ptr(y), w.m, w.k, _stream()))
     return y
@@ -151,8 +171,16 @@ def qgemv_fp8(w: QWeight, x, y=None):
     return y
 
 
+def _row_layout(w: QWeight) -> None:
+    if w.layout != LAYOUT_ROWS:
+        raise QGError(-4, "the single-token entry points take the row layout; use qgemm_rows")
+
+
 def qgemv(w: QWeight, x, y=None):
-    """The single-token GEMV entry point of w's type."""
+    """The single-token GEMV entry point of w's type (qgemm_rows with one row for a
+    tiled weight: the same kernel and bits)."""
+    if w.layout != LAYOUT_ROWS:
+        return qgemm_rows(w, x.reshape(1, -1), None if y is None else y.reshape(1, -1)).reshape(-1)
     f = {Q4_K: qgemv_q4k, Q5_K: qgemv_q5k, Q6_K: qgemv_q6k, NVFP4: qgemv_nvfp4, FP8: qgemv_fp8}[w.type]
     return f(w, x, y)
 

@@ -58,7 +58,10 @@ constexpr int64_t kMaxK = (int64_t)1 << 20;
 int check_weight(const qg_weight *w, const char *name) {
     if (!w) return fail(QG_ERR_NULL, "%s: weight descriptor is NULL", name);
     if (!known_type(w->type)) return fail(QG_ERR_TYPE, "%s: unknown type %d", name, w->type);
-    if (w->reserved != 0) return fail(QG_ERR_TYPE, "%s: reserved field must be 0", name);
+    if (w->layout != QG_LAYOUT_ROWS && w->layout != QG_LAYOUT_TILES)
+        return fail(QG_ERR_TYPE, "%s: unknown layout %d", name, w->layout);
+    if (w->layout == QG_LAYOUT_TILES && has_scales(w->type))
+        return fail(QG_ERR_TYPE, "%s: the tiled layout is for the K-quants only", name);
     if (!w->data) return fail(QG_ERR_NULL, "%s: data is NULL", name);
     if (has_scales(w->type) && !w->scales) return fail(QG_ERR_NULL, "%s: %s scales are NULL", name, type_name(w->type));
     if (w->m < 1 || w->m > kMaxM) return fail(QG_ERR_SHAPE, "%s: m = %lld out of range", name, (long long)w->m);
@@ -254,6 +257,7 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         g.type = w[s]->type;
         g.m = (int32_t)w[s]->m;
         g.ks = ks[s];
+        g.tiled = w[s]->layout == QG_LAYOUT_TILES;
         g.wg_begin = grid;
         if (sw) {
             g.data2 = (const uint8_t *)w[1]->data;
@@ -401,10 +405,34 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, f
         return rc;
     if (wg->k != wu->k || wg->m != wu->m)
         return fail(QG_ERR_SHAPE, "swiglu pair: gate and up must have the same m and k");
-    if (wg->type != wu->type) return fail(QG_ERR_TYPE, "swiglu pair: gate and up must have the same type");
+    if (wg->type != wu->type || wg->layout != wu->layout)
+        return fail(QG_ERR_TYPE, "swiglu pair: gate and up must have the same type and layout");
     const qg_weight *ws[2] = {wg, wu};
     float *ys[2] = {h, h};
     return run_mma(ws, ys, nullptr, 2, x, n, qg::MODE_SWIGLU, stream);
+}
+
+int64_t qg_tiles_bytes(const qg_weight *w) {
+    int rc;
+    if ((rc = check_weight(w, "w"))) return rc;
+    if (has_scales(w->type)) return fail(QG_ERR_TYPE, "w: the tiled layout is for the K-quants only");
+    return (w->m + 15) / 16 * 16 * qg_row_bytes(w->type, w->k);
+}
+
+int qg_pack_tiles(const qg_weight *w, void *dst, void *stream) {
+    int rc;
+    if ((rc = check_weight(w, "w"))) return rc;
+    if (w->layout != QG_LAYOUT_ROWS) return fail(QG_ERR_TYPE, "w: the source must be in the row layout");
+    if (has_scales(w->type)) return fail(QG_ERR_TYPE, "w: the tiled layout is for the K-quants only");
+    if (!dst) return fail(QG_ERR_NULL, "dst is NULL");
+    if (!aligned(dst, 16)) return fail(QG_ERR_ALIGN, "dst is not 16-byte aligned");
+    const int64_t row_bytes = qg_row_bytes(w->type, w->k);
+    const int sbytes = (int)(row_bytes / (w->k / 256));
+    hipError_t e = qg::launch_pack_tiles((const uint8_t *)w->data, (uint8_t *)dst, w->m, row_bytes, sbytes,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+    g_err.clear();
+    return QG_OK;
 }
 
 int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *stream) {
@@ -422,6 +450,7 @@ int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *
     a.n = n;
     a.k = (int32_t)w->k;
     a.type = w->type;
+    a.tiled = w->layout == QG_LAYOUT_TILES;
     // Largest tile that still gives every CU a workgroup (256 CUs).  Measured at
     // 512 tokens: the 128x128 tile beats 128x64 by 15% on the 9728-row matrix
     // (304 workgroups), and the next smaller tile wins once 128x128 leaves CUs idle.
@@ -454,6 +483,7 @@ int qdequant(const qg_weight *w, float *out, void *stream) {
     a.k = (int32_t)w->k;
     a.nb = (int32_t)(w->k / 256);
     a.type = w->type;
+    a.tiled = w->layout == QG_LAYOUT_TILES;
     hipError_t e = qg::launch_dequant(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
     g_err.clear();

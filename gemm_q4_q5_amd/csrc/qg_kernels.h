@@ -23,10 +23,14 @@ struct DequantArgs {
     int32_t k;
     int32_t nb;
     int32_t type;
-    int32_t pad;
+    int32_t tiled;   // K-quants: 16-row tiles (qg_weight.layout = QG_LAYOUT_TILES)
 };
 
 hipError_t launch_dequant(const DequantArgs &a, hipStream_t st);
+// Copy of a row-major K-quant matrix in 16-row tiles (16 * ceil(m/16) rows; the rows
+// past m repeat row m-1).
+hipError_t launch_pack_tiles(const uint8_t *src, uint8_t *dst, int64_t m, int64_t row_bytes, int sbytes,
+                             hipStream_t st);
 
 constexpr int kReadMaxRegions = 3;
 constexpr int kReadSlots = 64;         // XOR accumulators of the read probe ...

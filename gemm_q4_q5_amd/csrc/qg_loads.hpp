@@ -113,7 +113,17 @@ __device__ __forceinline__ RawF4 load_f4(const uint8_t *codes, const uint8_t *sc
 }
 
 // ---------------------------------------------------------------------------
-// The raw chunk type and loader of a weight type.
+// Superblock b of row r of a K-quant matrix of S-byte superblocks: rows one after
+// another (tiled = 0), or tiles of 16 rows in which superblock b of the tile's 16 rows
+// is stored contiguously (tiled = 1: ((r/16 * nb + b) * 16 + r%16) * S).
+__device__ __forceinline__ const uint8_t *kq_block(const uint8_t *data, int64_t row_bytes, int S, int64_t r, int b,
+                                                   int tiled) {
+    if (!tiled) return data + r * row_bytes + (int64_t)b * S;
+    const int64_t nb = row_bytes / S;
+    return data + (((r >> 4) * nb + b) * 16 + (r & 15)) * (int64_t)S;
+}
+
+// The raw chunk type and loader of a weight type (tiled: K-quants only).
 template <int T>
 struct Loader;
 
@@ -121,8 +131,8 @@ template <>
 struct Loader<T_Q4_K> {
     typedef RawKq Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
-                                               int b, int c) {
-        return load_kq(false, data + r * row_bytes + (int64_t)b * 144, c);
+                                               int b, int c, int tiled) {
+        return load_kq(false, kq_block(data, row_bytes, 144, r, b, tiled), c);
     }
 };
 
@@ -130,8 +140,8 @@ template <>
 struct Loader<T_Q5_K> {
     typedef RawKq Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
-                                               int b, int c) {
-        return load_kq(true, data + r * row_bytes + (int64_t)b * 176, c);
+                                               int b, int c, int tiled) {
+        return load_kq(true, kq_block(data, row_bytes, 176, r, b, tiled), c);
     }
 };
 
@@ -139,8 +149,8 @@ template <>
 struct Loader<T_Q6_K> {
     typedef RawQ6 Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
-                                               int b, int c) {
-        return load_q6(data + r * row_bytes + (int64_t)b * 210, c);
+                                               int b, int c, int tiled) {
+        return load_q6(kq_block(data, row_bytes, 210, r, b, tiled), c);
     }
 };
 
@@ -148,7 +158,7 @@ template <>
 struct Loader<T_NVFP4> {
     typedef RawF4 Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *scales, int64_t row_bytes,
-                                               int64_t r, int b, int c) {
+                                               int64_t r, int b, int c, int) {
         return load_f4(data + r * row_bytes + (int64_t)b * 128, scales + r * (row_bytes / 8) + (int64_t)b * 16, c);
     }
 };
@@ -157,7 +167,7 @@ template <>
 struct Loader<T_FP8> {
     typedef RawF8 Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *scales, int64_t row_bytes,
-                                               int64_t r, int b, int c) {
+                                               int64_t r, int b, int c, int) {
         return load_f8(data + r * row_bytes + (int64_t)b * 256, scales + (r >> 7) * (row_bytes / 64), b, c);
     }
 };

@@ -115,23 +115,26 @@ struct MRawOf<T_FP8> {
 // boundary.  Every load is issued from the 4-byte-aligned address below the data;
 // the dword after each run, which the byte-pairing permute needs to realign, is
 // the first dword of another lane's run (q6_extras).
+// row: the row's superblock 0; sbs: bytes from one of the row's superblocks to the
+// next (the superblock size, or 16 times it in the 16-row tiled layout).
 template <int T>
-__device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, const uint8_t *srow, int b, int g) {
+__device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, const uint8_t *srow, int b, int g,
+                                                          int sbs) {
     typename MRawOf<T>::type r;
     if constexpr (T == T_Q4_K) {
-        const uint8_t *blk = row + (int64_t)b * 144;
+        const uint8_t *blk = row + (int64_t)b * sbs;
         r.hdr = mld16(blk);
         r.q0 = mld16(blk + 16 + 32 * g);
         r.q1 = mld16(blk + 32 + 32 * g);
     } else if constexpr (T == T_Q5_K) {
-        const uint8_t *blk = row + (int64_t)b * 176;
+        const uint8_t *blk = row + (int64_t)b * sbs;
         r.hdr = mld16(blk);
         r.h0 = mld16(blk + 16);
         r.h1 = mld16(blk + 32);
         r.q0 = mld16(blk + 48 + 32 * g);
         r.q1 = mld16(blk + 64 + 32 * g);
     } else if constexpr (T == T_Q6_K) {
-        const uint8_t *blk = row + (int64_t)b * 210;
+        const uint8_t *blk = row + (int64_t)b * sbs;
         const int s = g >> 1, h = g & 1;
         const uint32_t mis = (uint32_t)((uintptr_t)blk & 3u);   // 0 or 2
         const uint8_t *base = blk - mis;
@@ -563,7 +566,7 @@ __device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, in
 // turn; every wave steps through every chunk (two barriers per step), whether or
 // not it has superblocks there, so all waves meet the same barriers.
 template <int T, int NT, int NG, int NP, int D>
-__device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool dec, int g, int t,
+__device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int sbs, bool dec, int g, int t,
                                          const uint8_t *const (&wr)[NT], const uint8_t *const (&sr)[NT], uint4 *lds,
                                          f4 (&acc)[NP][NT][NG]) {
     typedef typename MRawOf<T>::type Raw;
@@ -617,7 +620,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool 
             const int q = q0 + lane;
             if (cnt > 0) xhalf_fetch<T>(A, q < hq ? q : hq - 1, kw, KW, X);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kw, lastb), g);
+            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kw, lastb), g, sbs);
             if (cnt > 0) xhalf_commit<T>(q, q < hq, X, xu);   // LDS order within a wave: no barrier
         }
 #pragma unroll
@@ -625,7 +628,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool 
             if (u + 1 < D) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(sb(u + 1), lastb), g);
+                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(sb(u + 1), lastb), g, sbs);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (u < cnt) {   // scalar branch
@@ -642,7 +645,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool 
 #pragma unroll
         for (int u = 0; u < D; ++u)
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(sb(u), lastb), g);
+            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(sb(u), lastb), g, sbs);
     });
     __syncthreads();
     int chunk = 0;
@@ -664,7 +667,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, bool 
             }
             if (it + D < cnt) {   // refill only with a superblock the wave still serves
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], sr[i], min(sb(it + D), lastb), g);
+                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], sr[i], min(sb(it + D), lastb), g, sbs);
             }
         }
     }
@@ -717,11 +720,16 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 
     const uint8_t *wr[NT];
     const uint8_t *sr[NT];
+    // K-quant superblock bytes; in the 16-row tiled layout a row's superblocks are
+    // 16 of them apart, the row's first at ((r/16) * nb * 16 + r%16) * sbytes.
+    const int sbytes = S.type == T_Q4_K ? 144 : (S.type == T_Q5_K ? 176 : (S.type == T_Q6_K ? 210 : 0));
+    const int sbs = S.tiled ? 16 * sbytes : sbytes;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t r = rows[i] < S.m ? rows[i] : S.m - 1;   // rows past m read row m-1; results dropped
         const bool second = up != 0;
-        wr[i] = (second ? S.data2 : S.data) + r * S.row_bytes;
+        const int64_t roff = S.tiled ? ((r >> 4) * A.nb * 16 + (r & 15)) * sbytes : r * S.row_bytes;
+        wr[i] = (second ? S.data2 : S.data) + roff;
         const uint8_t *sc = second ? S.scales2 : S.scales;
         // NVFP4: one e4m3 scale per 16 weights of the row; FP8: the bf16 scale row
         // of the row's 128-row block (K/128 scales of 2 bytes).
@@ -736,15 +744,15 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 #pragma unroll
             for (int q = 0; q < NG; ++q) ph[a][i][q] = (f4){0.f, 0.f, 0.f, 0.f};
     if ((TS & TS_Q4) && S.type == T_Q4_K)
-        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_Q5) && S.type == T_Q5_K)
-        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_Q6) && S.type == T_Q6_K)
-        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_F4) && S.type == T_NVFP4)
-        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_F8) && S.type == T_FP8)
-        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
 
     // The KS phase partials of a row tile, added in phase order:
     //     y = (((p0 + p1) + p2) + ...) + p(KS-1).

@@ -31,7 +31,7 @@ struct MSeg {
                              //    ceil(nb/ks) <= kMmaDepth (2 with two tiles per wave),
                              //    8*n*ceil(nb/ks) <= 64*kMmaDecRounds, and LDS for
                              //    wv*ceil(nb/ks)*n*576 bytes after the 144 of zeros)
-    int32_t pad;
+    int32_t tiled;           // K-quants: 16-row tiled layout (qg_weight.layout = QG_LAYOUT_TILES)
 };
 
 struct MmaArgs {

@@ -14,6 +14,8 @@ struct PrefillArgs {
     int64_t m, n;
     int32_t k;
     int32_t type;
+    int32_t tiled;           // K-quants: 16-row tiles (qg_weight.layout = QG_LAYOUT_TILES)
+    int32_t pad;
 };
 
 // bm x bn tile per workgroup: (128, 128), (128, 64) or (64, 64).

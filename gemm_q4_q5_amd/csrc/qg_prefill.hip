@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
 template <int T>
 __device__ __forceinline__ typename Loader<T>::Raw p_load(const PrefillArgs &A, int64_t r, int kt, int hf) {
     const int b = kt >> 1, c = 2 * (kt & 1) + hf;
-    return Loader<T>::load(A.data, A.scales, A.row_bytes, r, b, c);
+    return Loader<T>::load(A.data, A.scales, A.row_bytes, r, b, c, A.tiled);
 }
 
 // Write the task's 64 weights (fp16, one rounding of the exact fp32 value) into

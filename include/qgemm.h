@@ -37,7 +37,13 @@
  *    Weight value: Q4_K/Q5_K  d*sc[j]*q - dmin*min[j]  ([PF] Path E);
  *                  Q6_K       d*sc[j]*(q - 32);
  *                  NVFP4      e2m1(code) * e4m3(scale)  ([TK] NVFP4).
- *    Row r of a K-quant weight starts at data + r * qg_row_bytes(type, k).
+ *    Row r of a K-quant weight starts at data + r * qg_row_bytes(type, k)
+ *    (QG_LAYOUT_ROWS, the layout the superblocks are stored in), or, in the
+ *    16-row tiled layout (QG_LAYOUT_TILES, made by qg_pack_tiles), superblock b of
+ *    row r sits at data + ((r/16 * (k/256) + b) * 16 + r%16) * S, S the superblock
+ *    size: superblock b of 16 consecutive rows is contiguous, so a wave that
+ *    streams 16 rows reads one run.  The values are the same; so are the bits of
+ *    every product.
  *  - k must be a multiple of 256 for every type (one superblock; for NVFP4 one
  *    block of 16 scales).  m >= 1.
  *  - Alignment: data, scales and x 16-byte aligned; y and resid 4-byte aligned.
@@ -91,13 +97,16 @@ typedef enum {
 
 #define QG_MAX_ROWS 32       /* largest n of the row-invariant calls ([KN] GEMM_MAX_BATCH) */
 
+#define QG_LAYOUT_ROWS  0    /* rows one after another, as stored               */
+#define QG_LAYOUT_TILES 1    /* K-quants in 16-row tiles (see qg_pack_tiles)     */
+
 /* A quantized weight matrix (m rows of k weights).  `scales` is used by NVFP4 and
  * FP8 and must be non-NULL (16-byte aligned) for them; it is ignored for the
  * K-quants.  FP8: data = e4m3 codes [m][k] (OCP E4M3FN, one byte per weight), scales
  * = bf16 [ceil(m/128)][k/128] row-major, weight (r, c) = code * scale[r/128][c/128]. */
 typedef struct qg_weight {
     int32_t type;        /* a qg_type                                   */
-    int32_t reserved;    /* must be 0                                   */
+    int32_t layout;      /* QG_LAYOUT_ROWS (0) or QG_LAYOUT_TILES (1)    */
     const void *data;    /* superblocks, or NVFP4 / FP8 codes           */
     const void *scales;  /* NVFP4 e4m3 [m][k/16]; FP8 bf16 [m/128][k/128] */
     int64_t m;           /* rows (output features)                      */
@@ -107,6 +116,19 @@ typedef struct qg_weight {
 /* Bytes of one stored weight row (NVFP4 and FP8: of the codes only); -1 if the
  * type is unknown or k is not a multiple of 256. */
 int64_t qg_row_bytes(int32_t type, int64_t k);
+
+/*
+ * The 16-row tiled layout of a K-quant matrix (an MI355X-side layout choice, not a
+ * format of the pages): qg_tiles_bytes gives the size of the tiled copy of w,
+ * 16 * ceil(m/16) * qg_row_bytes (the rows past m in the last tile repeat row
+ * m-1), or a negative error (QG_ERR_TYPE for NVFP4/FP8).  qg_pack_tiles writes that
+ * copy of w (which must be in QG_LAYOUT_ROWS) to dst (device, 16-byte aligned, owned
+ * by the caller; must not overlap w->data); describe it with layout =
+ * QG_LAYOUT_TILES and the same type, m and k.  Every call accepts both layouts
+ * (the single-token qgemv_q4k/q5k/q6k take the row layout only).
+ */
+int64_t qg_tiles_bytes(const qg_weight *w);
+int qg_pack_tiles(const qg_weight *w, void *dst, void *stream);
 
 /* Static text for a status code. */
 const char *qg_status_str(int status);

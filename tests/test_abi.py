@@ -24,6 +24,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("qgemv_q4k", "qgemv_q5k", "qgemv_q6k", "qgemv_nvfp4", "qgemv_fp8", "qgemm_rows", "qgemv_add",
                  "qgemv_pair", "qgemv_triple", "qgemv_pair_swiglu", "qdequant", "qg_row_bytes",
+                 "qg_tiles_bytes", "qg_pack_tiles",
                  "qg_status_str", "qg_last_error"):
         assert want in names
 
@@ -53,15 +54,17 @@ def test_status_strings():
 FAKE = 0x10000  # 64 KiB: 16-byte aligned, never dereferenced (validation fails first)
 
 
-def w(type_=12, data=FAKE, scales=None, m=8, k=512, reserved=0):
-    c = CWeight(type_, reserved, data, scales, m, k)
+def w(type_=12, data=FAKE, scales=None, m=8, k=512, layout=0):
+    c = CWeight(type_, layout, data, scales, m, k)
     return ctypes.byref(c), c
 
 
 @pytest.mark.parametrize("case,code", [
     (dict(data=None), -1),
     (dict(type_=7), -4),
-    (dict(reserved=1), -4),
+    (dict(layout=2), -4),
+    (dict(type_=1001, scales=FAKE, layout=1), -4),
+    (dict(type_=1002, scales=FAKE, layout=1), -4),
     (dict(m=0), -2),
     (dict(k=300), -2),
     (dict(k=0), -2),
@@ -138,3 +141,21 @@ def test_stream_read_validation(ptrs, sizes, nreg, out, code):
     p, b = _regions(ptrs, sizes)
     assert L.qg_stream_read(p, b, nreg, out, None) == code
     assert L.qg_last_error() != b""
+
+
+def test_tiles_bytes_and_pack_validation():
+    L = qg.lib()
+    a, _a = w(type_=12, m=17, k=512)                  # 2 tiles of 16 rows, 288-byte rows
+    assert L.qg_tiles_bytes(a) == 32 * 288
+    b, _b = w(type_=14, m=2560, k=9728)
+    assert L.qg_tiles_bytes(b) == 2560 * 38 * 210
+    f, _f = w(type_=1001, scales=FAKE)
+    assert L.qg_tiles_bytes(f) == -4
+    assert L.qg_pack_tiles(a, None, None) == -1
+    assert L.qg_pack_tiles(a, FAKE + 8, None) == -5
+    t, _t = w(type_=12, m=17, k=512, layout=1)
+    assert L.qg_pack_tiles(t, FAKE, None) == -4       # the source must be in the row layout
+    assert L.qg_pack_tiles(f, FAKE, None) == -4
+    g, _g = w(type_=12, m=8, k=512)
+    u, _u = w(type_=12, m=8, k=512, layout=1)
+    assert L.qgemv_pair_swiglu(g, u, FAKE, FAKE, 1, None) == -4   # gate and up in different layouts
