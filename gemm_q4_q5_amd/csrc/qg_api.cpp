@@ -451,18 +451,21 @@ int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *
     a.k = (int32_t)w->k;
     a.type = w->type;
     a.tiled = w->layout == QG_LAYOUT_TILES;
-    // Largest tile that still gives every CU a workgroup (256 CUs).  Measured at
-    // 512 tokens: the 128x128 tile beats 128x64 by 15% on the 9728-row matrix
-    // (304 workgroups), and the next smaller tile wins once 128x128 leaves CUs idle.
+    // 128x128 tiles when they give every CU a workgroup (256 CUs); else 128x64 tiles
+    // when they fill 160..256 CUs in one round (their two LDS tile pairs, 96 KB,
+    // leave room for one workgroup per CU); else 64x64 (two per CU).  Measured at
+    // 512 tokens: the 9728-row matrix on 128x128 tiles (304 workgroups) 67 us
+    // against 80 us on 128x64; the 2560 x 9728 matrix on 128x64 (160 workgroups)
+    // 111 us against 119 us on 64x64; at 256 tokens the 4096-row matrix on 64x64
+    // (256 workgroups) beats 128x64 (128).
     int bm = 64, bn = 64;
-    const int tiles[3][2] = {{128, 128}, {128, 64}, {64, 64}};
-    for (auto &t : tiles) {
-        const int64_t wgs = ((w->m + t[1] - 1) / t[1]) * ((n + t[0] - 1) / t[0]);
-        if (wgs >= 256) {
-            bm = t[0];
-            bn = t[1];
-            break;
-        }
+    const int64_t rt128 = (w->m + 127) / 128, rt64 = (w->m + 63) / 64, tt128 = (n + 127) / 128;
+    if (rt128 * tt128 >= 256) {
+        bm = 128;
+        bn = 128;
+    } else if (rt64 * tt128 >= 160 && rt64 * tt128 <= 256) {
+        bm = 128;
+        bn = 64;
     }
     hipError_t e = qg::launch_prefill(a, bm, bn, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

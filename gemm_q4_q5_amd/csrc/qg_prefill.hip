@@ -5,11 +5,20 @@
 // prefill GEMM whose per-(row, sub-block) scales are decoded once and shared, and
 // whose dequantized weight tile is shared by every wave of the block (E5).  Here
 // a workgroup of four waves owns a BM x BN tile of Y (tokens x weight rows) and
-// walks K in 128-wide steps: it stages X[BM][128] and the dequantized W[BN][128]
-// (fp16: the exact weight rounded once, to nearest even; |error| <= 2^-11 |w|) in LDS,
-// then each wave runs v_mfma_f32_16x16x32_f16 over its (BM/2) x (BN/2) sub-tile
-// with fp32 accumulation.  The next step's global loads are issued before the
-// current step's MFMAs.  No row-invariance contract (TandemLLM Kernels page,
+// walks K in 128-wide steps through LDS: X[BM][128] as stored (fp16) and the
+// dequantized W[BN][128] (fp16: the exact weight rounded once, to nearest even;
+// |error| <= 2^-11 |w|); each wave runs v_mfma_f32_16x16x32_f16 over its
+// (BM/2) x (BN/2) sub-tile with fp32 accumulation.
+//
+// With two LDS tile pairs (the 128x64 and 64x64 tiles) the steps are pipelined
+// with one barrier each: while step s's MFMAs drain, step s+1's X (loaded into
+// registers during step s-1) is written and its weights dequantized into the
+// other pair, and step s+2's loads are issued; each wave reads the next 32-wide
+// slice's fragments while the current slice's MFMAs run.  The 128x128 tile (and
+// 64x64 in grids of more than 512 workgroups) uses one pair and two barriers per
+// step, its next step's loads in flight during the MFMAs.  Loads past the last token or weight row are clamped to the
+// last one (every address stays in bounds, no branches in the loop); those rows of
+// the tile are never stored.  No row-invariance contract (TandemLLM Kernels page,
 // "Prefill kernels"): the result is deterministic, but not the decode kernel's bits.
 #include "qg_loads.hpp"
 #include "qg_prefill.h"
@@ -19,8 +28,12 @@ namespace qg {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int KT = 128;       // K per step: half a superblock
-constexpr int KP = KT + 8;    // LDS row pitch in halves (16 bytes of padding)
+constexpr int KT = 128;   // K per step: half a superblock
+
+// LDS tiles hold rows of KT halves, 16 chunks of 16 bytes; chunk c of row r sits at
+// chunk c ^ (r & 15), so the 16 lanes of a fragment read (16 rows, one chunk each)
+// hit 16 different 16-byte bank groups with no padding.
+__device__ __forceinline__ int swz(int row, int c) { return row * 16 + (c ^ (row & 15)); }
 
 // Pack two fp32 into an fp16 pair, round to nearest even.
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
@@ -38,9 +51,10 @@ __device__ __forceinline__ typename Loader<T>::Raw p_load(const PrefillArgs &A, 
 }
 
 // Write the task's 64 weights (fp16, one rounding of the exact fp32 value) into
-// the LDS row of the step, at their K offsets within the step.
+// row `row` of the LDS weight tile, at their K offsets within the step (in 16-byte
+// chunks, swizzled).
 template <int T>
-__device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt, int hf, _Float16 *wrow) {
+__device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt, int hf, uint4 *tile, int row) {
     const int c = 2 * (kt & 1) + hf;
     if (T == T_Q4_K || T == T_Q5_K) {
         // chunk c: sub-block 2c at step offsets 64hf + 0..31, 2c+1 at 64hf + 32..63
@@ -67,12 +81,10 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
             hi[2 * i] = pack_h2(__builtin_fmaf(cf.a1, (float)p2.x, cf.b1), __builtin_fmaf(cf.a1, (float)p2.y, cf.b1));
             hi[2 * i + 1] = pack_h2(__builtin_fmaf(cf.a1, (float)p3.x, cf.b1), __builtin_fmaf(cf.a1, (float)p3.y, cf.b1));
         }
-        uint4 *dl = reinterpret_cast<uint4 *>(wrow + 64 * hf);
-        uint4 *dh = reinterpret_cast<uint4 *>(wrow + 64 * hf + 32);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            dl[q] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
-            dh[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
+            tile[swz(row, 8 * hf + q)] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
+            tile[swz(row, 8 * hf + 4 + q)] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
         }
     } else if (T == T_Q6_K) {
         // half s of the superblock: group g at step offsets 32g + 16hf + 0..15
@@ -101,9 +113,8 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            uint4 *d = reinterpret_cast<uint4 *>(wrow + 32 * g + 16 * hf);
-            d[0] = make_uint4(out[g][0], out[g][1], out[g][2], out[g][3]);
-            d[1] = make_uint4(out[g][4], out[g][5], out[g][6], out[g][7]);
+            tile[swz(row, 4 * g + 2 * hf)] = make_uint4(out[g][0], out[g][1], out[g][2], out[g][3]);
+            tile[swz(row, 4 * g + 2 * hf + 1)] = make_uint4(out[g][4], out[g][5], out[g][6], out[g][7]);
         }
     } else if (T == T_FP8) {
         // FP8 chunk c: 64 codes at step offsets 64hf + 0..63; code * scale is exact in
@@ -112,47 +123,74 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
         const float sc = bf16_lo(Q.sc);
         const uint32_t qw[16] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w,
                                  Q.q2.x, Q.q2.y, Q.q2.z, Q.q2.w, Q.q3.x, Q.q3.y, Q.q3.z, Q.q3.w};
-        uint4 *d = reinterpret_cast<uint4 *>(wrow + 64 * hf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t a = qw[2 * i], b = qw[2 * i + 1];
-            d[i] = make_uint4(pack_h2(e4m3_at(a, 0) * sc, e4m3_at(a, 1) * sc), pack_h2(e4m3_at(a, 2) * sc, e4m3_at(a, 3) * sc),
+            tile[swz(row, 8 * hf + i)] = make_uint4(pack_h2(e4m3_at(a, 0) * sc, e4m3_at(a, 1) * sc), pack_h2(e4m3_at(a, 2) * sc, e4m3_at(a, 3) * sc),
                               pack_h2(e4m3_at(b, 0) * sc, e4m3_at(b, 1) * sc), pack_h2(e4m3_at(b, 2) * sc, e4m3_at(b, 3) * sc));
         }
     } else {
         // NVFP4 chunk c: 64 codes at step offsets 64hf + 0..63, four scales
         const RawF4 &Q = reinterpret_cast<const RawF4 &>(R);
         const uint32_t qw[8] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w};
-        uint4 *d = reinterpret_cast<uint4 *>(wrow + 64 * hf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const _Float16 sh = (_Float16)e4m3_at(Q.sc, i >> 1);   // e4m3 values are exact in fp16
             uint32_t v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = as_u32(as_h2(fp4_pair(qw[i], j)) * (h2){sh, sh});   // exact
-            d[i] = make_uint4(v[0], v[1], v[2], v[3]);
+            tile[swz(row, 8 * hf + i)] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
 }
 
-template <int T, int BM, int BN>
+// DB: double-buffered tiles, one barrier per step (see the header); otherwise one
+// tile pair and two barriers per step: write step s's X and weights, barrier,
+// issue step s+1's loads, MFMAs, barrier.  The 128x128 tile keeps the single buffer:
+// with two, its registers no longer fit and the accumulators are shuffled between
+// register files every step (measured 25 % slower); the smaller tiles gain ~10 %.
+template <int T, int BM, int BN, bool DB>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
-    constexpr int TM = BM / 32, TN = BN / 32;      // 16x16 MFMA tiles per wave (2 x 2 waves)
-    constexpr int XV = BM * KT / 8 / 256;          // 16-byte X loads per thread per step
-    __shared__ __align__(16) _Float16 xs[BM * KP];
-    __shared__ __align__(16) _Float16 ws[BN * KP];
+    constexpr int TM = BM / 32, TN = BN / 32;   // 16x16 MFMA tiles per wave (2 x 2 waves)
+    constexpr int XC = BM * 16, WC = BN * 16;   // 16-byte chunks per X / W stage
+    constexpr int XL = XC / 256;                // 16-byte X loads per thread per step
+    extern __shared__ uint4 lds[];              // X stage(s), then W stage(s)
+    uint4 *const xst = lds;
+    uint4 *const wst = lds + (DB ? 2 : 1) * XC;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.y * BM;   // first token
     const int64_t n0 = (int64_t)blockIdx.x * BN;   // first weight row
-    const int nk = A.k / KT;
+    const int nk = A.k / KT;                       // even: k is a multiple of 256
+    const int last = nk - 1;
 
-    // dequant task of this thread (BN rows x 2 chunks per step; threads beyond idle)
+    // Dequant task of this thread: row drow, half dhf of the step's 128 weights
+    // (BN rows x 2 halves; threads beyond 2 BN idle, whole waves).  Rows past m
+    // read row m-1.
     const bool dq = tid < 2 * BN;
     const int drow = tid >> 1, dhf = tid & 1;
-    const int64_t wr = n0 + drow;
-    const bool wvalid = dq && wr < A.m;
+    const int64_t wr = n0 + drow < A.m ? n0 + drow : A.m - 1;
+
+    // X: unit v of this thread is chunk c = tid % 16 of row tid / 16 + 16 v; tokens
+    // past n read token n-1.
+    const int64_t kv = A.k / 8;   // 16-byte units per X row
+    const u32x4 *xt = reinterpret_cast<const u32x4 *>(A.x) + m0 * kv + (tid & 15);
+    int xo[XL];
+#pragma unroll
+    for (int v = 0; v < XL; ++v) {
+        const int64_t t = m0 + (tid >> 4) + 16 * v;
+        xo[v] = (int)(((t < A.n ? t : A.n - 1) - m0) * kv);
+    }
+    auto load_x = [&](u32x4 (&xv)[XL], int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < XL; ++v) xv[v] = xt[xo[v] + kt * (KT / 8)];
+    };
+    auto store_x = [&](const u32x4 (&xv)[XL], int stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < XL; ++v)
+            *reinterpret_cast<u32x4 *>(xst + stage * XC + swz((tid >> 4) + 16 * v, tid & 15)) = xv[v];
+    };
 
     f4 acc[TM][TN];
 #pragma unroll
@@ -160,52 +198,87 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    const uint4 *xg = reinterpret_cast<const uint4 *>(A.x);
-    uint4 xv[XV];
-    typename Loader<T>::Raw raw;
-    auto fetch = [&](int kt) {
+    const int arow = wm * (BM / 2) + (lane & 15), brow = wn * (BN / 2) + (lane & 15);
+    if constexpr (!DB) {
+        typename Loader<T>::Raw raw;
+        u32x4 xv[XL];
+        if (dq) raw = p_load<T>(A, wr, 0, dhf);
+        load_x(xv, 0);
+        for (int s = 0; s < nk; ++s) {
+            __syncthreads();   // the previous step's readers are done
+            store_x(xv, 0);
+            if (dq) p_store<T>(raw, s, dhf, wst, drow);
+            __syncthreads();
+            if (s + 1 < nk) {   // in flight during this step's MFMAs
+                load_x(xv, s + 1);
+                if (dq) raw = p_load<T>(A, wr, s + 1, dhf);
+            }
 #pragma unroll
-        for (int v = 0; v < XV; ++v) {
-            const int i = tid + 256 * v;          // 16-byte unit of the X tile
-            const int row = i >> 4, col = i & 15;  // 16 units per 128-wide row
-            const int64_t t = m0 + row;
-            xv[v] = t < A.n ? xg[(t * A.k + (int64_t)kt * KT) / 8 + col] : make_uint4(0, 0, 0, 0);
-        }
-        if (wvalid) raw = p_load<T>(A, wr, kt, dhf);
-    };
-    fetch(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();   // the previous step's readers are done
+            for (int ks = 0; ks < KT / 32; ++ks) {
+                const int c = 4 * ks + (lane >> 4);
+                h8 af[TM], bf[TN];
 #pragma unroll
-        for (int v = 0; v < XV; ++v) {
-            const int i = tid + 256 * v;
-            *reinterpret_cast<uint4 *>(xs + (i >> 4) * KP + (i & 15) * 8) = xv[v];
-        }
-        if (dq) {
-            _Float16 *wrow = ws + drow * KP;
-            if (wvalid) {
-                p_store<T>(raw, kt, dhf, wrow);
-            } else {   // rows past m: zeros (NVFP4/K-quant halves each cover 64 of the 128)
-                for (int q = 0; q < 8; ++q) reinterpret_cast<uint4 *>(wrow)[8 * dhf + q] = make_uint4(0, 0, 0, 0);
+                for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const h8 *>(xst + swz(arow + 16 * i, c));
+#pragma unroll
+                for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const h8 *>(wst + swz(brow + 16 * j, c));
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
         }
-        __syncthreads();
-        if (kt + 1 < nk) fetch(kt + 1);   // in flight during this step's MFMAs
-#pragma unroll
-        for (int ks = 0; ks < KT / 32; ++ks) {
-            h8 af[TM], bf[TN];
-            const int kof = ks * 32 + 8 * (lane >> 4);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const h8 *>(xs + (wm * (BM / 2) + 16 * i + (lane & 15)) * KP + kof);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const h8 *>(ws + (wn * (BN / 2) + 16 * j + (lane & 15)) * KP + kof);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    } else {
+        // One register slot per stream: loaded during step s, written to LDS during
+        // step s+1.  Step indexes past the end are clamped (redundant, in-bounds loads).
+        typename Loader<T>::Raw raw;
+        u32x4 xv[XL];
+        if (dq) raw = p_load<T>(A, wr, 0, dhf);
+        load_x(xv, 0);
+        store_x(xv, 0);
+        if (dq) {
+            p_store<T>(raw, 0, dhf, wst, drow);
+            raw = p_load<T>(A, wr, 1, dhf);
+        }
+        load_x(xv, 1);
+
+        for (int s = 0; s < nk; ++s) {
+            // Every wave's part of step s's tiles is in LDS, and every wave is done
+            // with step s-1's tiles (rewritten below with step s+1).
+            __syncthreads();
+            const int p = s & 1;
+            const uint4 *xs = xst + p * XC;
+            const uint4 *ws = wst + p * WC;
+            h8 af[2][TM], bf[2][TN];
+    #pragma unroll
+            for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const h8 *>(xs + swz(arow + 16 * i, lane >> 4));
+    #pragma unroll
+            for (int j = 0; j < TN; ++j) bf[0][j] = *reinterpret_cast<const h8 *>(ws + swz(brow + 16 * j, lane >> 4));
+    #pragma unroll
+            for (int ks = 0; ks < KT / 32; ++ks) {
+                const int cur = ks & 1;
+                if (ks + 1 < KT / 32) {
+                    const int c = 4 * (ks + 1) + (lane >> 4);
+    #pragma unroll
+                    for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = *reinterpret_cast<const h8 *>(xs + swz(arow + 16 * i, c));
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j) bf[cur ^ 1][j] = *reinterpret_cast<const h8 *>(ws + swz(brow + 16 * j, c));
+                }
+    #pragma unroll
+                for (int i = 0; i < TM; ++i)
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
+            }
+            // step s+1 into the other tiles (last read in step s-1) while the last
+            // MFMAs drain, then load step s+2
+            const int s1 = s + 1 < last ? s + 1 : last, s2 = s + 2 < last ? s + 2 : last;
+            store_x(xv, p ^ 1);
+            load_x(xv, s2);
+            if (dq) {
+                p_store<T>(raw, s1, dhf, wst + (p ^ 1) * WC, drow);
+                raw = p_load<T>(A, wr, s2, dhf);
+            }
         }
     }
     // D tile (i, j): lane holds tokens 4*(lane/16)+e, weight row lane%16.
@@ -222,16 +295,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
         }
 }
 
+template <int T, int BM, int BN, bool DB>
+static hipError_t launch_tile(const PrefillArgs &A, hipStream_t st) {
+    const dim3 grid((unsigned)((A.m + BN - 1) / BN), (unsigned)((A.n + BM - 1) / BM));
+    const size_t lds = (size_t)(BM + BN) * 256 * (DB ? 2 : 1);
+    const void *fn = (const void *)prefill_kernel<T, BM, BN, DB>;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((prefill_kernel<T, BM, BN, DB>), grid, dim3(256), lds, st, A);
+    return hipGetLastError();
+}
+
 template <int T>
 static hipError_t launch_t(const PrefillArgs &A, int bm, int bn, hipStream_t st) {
-    const dim3 grid((unsigned)((A.m + bn - 1) / bn), (unsigned)((A.n + bm - 1) / bm));
-    if (bm == 128 && bn == 128)
-        hipLaunchKernelGGL((prefill_kernel<T, 128, 128>), grid, dim3(256), 0, st, A);
-    else if (bm == 128)
-        hipLaunchKernelGGL((prefill_kernel<T, 128, 64>), grid, dim3(256), 0, st, A);
-    else
-        hipLaunchKernelGGL((prefill_kernel<T, 64, 64>), grid, dim3(256), 0, st, A);
-    return hipGetLastError();
+    if (bm == 128 && bn == 128) return launch_tile<T, 128, 128, false>(A, st);
+    if (bm == 128) return launch_tile<T, 128, 64, true>(A, st);
+    // Two 64x64 tile pairs (64 KB) leave room for two workgroups per CU; past 512
+    // workgroups the single pair (32 KB) keeps them all resident at once.
+    if ((A.m + 63) / 64 * ((A.n + 63) / 64) > 512) return launch_tile<T, 64, 64, false>(A, st);
+    return launch_tile<T, 64, 64, true>(A, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs &A, int bm, int bn, hipStream_t st) {

@@ -21,10 +21,12 @@ TYPES = [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4, qg.FP8]
 
 
 @pytest.mark.parametrize("wt", TYPES)
-# The last two shapes are large enough for the 128x128 and 128x64 tiles (at least
-# 256 workgroups), ragged in both dimensions; the others take the 64x64 tile.
+# (2000, 256, 2050) takes the 128x128 tile (single-buffered loop), (1000, 512, 2000)
+# the 128x64 tile (pipelined loop), (1000, 256, 2100) the 64x64 tile in a grid of
+# more than 512 workgroups (single-buffered loop), all ragged in both dimensions;
+# the others take the 64x64 tile (pipelined loop).
 @pytest.mark.parametrize("m,k,n", [(300, 1024, 130), (64, 256, 1), (130, 768, 17), (1000, 512, 256),
-                                   (2000, 256, 2050), (1000, 512, 2000)])
+                                   (2000, 256, 2050), (1000, 512, 2000), (1000, 256, 2100)])
 def test_prefill_vs_oracle(wt, m, k, n):
     import torch
     print(f"prefill type={wt} m={m} k={k} n={n}", flush=True)
@@ -52,9 +54,10 @@ def test_prefill_deterministic():
     assert np.array_equal(a, b)
 
 
-# (m, k) with k tokens of an identity input: 64x64, 128x64 and 128x128 tiles.
+# (m, k) with k tokens of an identity input: the 64x64 tile pipelined and (1500 x
+# 2048, 768 workgroups) single-buffered, 128x64 and 128x128.
 @pytest.mark.parametrize("wt", TYPES)
-@pytest.mark.parametrize("m,k", [(300, 512), (2000, 1280), (2048, 2048)])
+@pytest.mark.parametrize("m,k", [(300, 512), (1500, 2048), (1250, 1280), (2048, 2048)])
 def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
     """x = I (k tokens): y[t][r] is the kernel's fp16 operand for w[r][t] (one
     nonzero product, exact in fp32), which must equal the oracle's exact weight
