@@ -42,9 +42,14 @@ LAYERS = 36
 
 
 def kernel_source_sha() -> str:
+    """Hash of the sources the decode products and their launch choice are built
+    from (the MFMA product kernels, their loads, device helpers and the C-ABI
+    launch code); the prefill, dequant and probe kernels are left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_q4_q5_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not (name.startswith("qg_mma") or name in ("qg_loads.hpp", "qg_device.hpp", "qg_api.cpp")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
