@@ -467,6 +467,8 @@ int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *
         bm = 128;
         bn = 64;
     }
+    if ((w->m + bn - 1) / bn * ((n + bm - 1) / bm) > 0x7fffffff)
+        return fail(QG_ERR_SHAPE, "m = %lld, n = %lld: more than 2^31 - 1 tiles", (long long)w->m, (long long)n);
     hipError_t e = qg::launch_prefill(a, bm, bn, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
     g_err.clear();

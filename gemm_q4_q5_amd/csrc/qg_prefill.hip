@@ -160,8 +160,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;   // first token
-    const int64_t n0 = (int64_t)blockIdx.x * BN;   // first weight row
+    // One-dimensional grid, row tiles fastest: (row tile, token tile) of this block.
+    const int64_t rtiles = (A.m + BN - 1) / BN;
+    const int64_t m0 = (int64_t)blockIdx.x / rtiles * BM;   // first token
+    const int64_t n0 = (int64_t)blockIdx.x % rtiles * BN;   // first weight row
     const int nk = A.k / KT;                       // even: k is a multiple of 256
     const int last = nk - 1;
 
@@ -297,7 +299,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
 
 template <int T, int BM, int BN, bool DB>
 static hipError_t launch_tile(const PrefillArgs &A, hipStream_t st) {
-    const dim3 grid((unsigned)((A.m + BN - 1) / BN), (unsigned)((A.n + BM - 1) / BM));
+    const int64_t blocks = (A.m + BN - 1) / BN * ((A.n + BM - 1) / BM);
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
     const size_t lds = (size_t)(BM + BN) * 256 * (DB ? 2 : 1);
     const void *fn = (const void *)prefill_kernel<T, BM, BN, DB>;
     if (lds > 65536) {

@@ -206,8 +206,10 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
  * n >= 1 and every weight type.  Each workgroup dequantizes its weight tile once
  * into fp16 in LDS (the exact weight rounded once, to nearest even; |error| <= 2^-11 |w|)
  * and multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
- * y fp32 [n][m].  Deterministic; no row-invariance contract ([TK] "Prefill
- * kernels": chunk kernels share work across rows and are checked by agreement).
+ * y fp32 [n][m].  n up to 2^30; QG_ERR_SHAPE if the call would need more than
+ * 2^31 - 1 tiles of Y (64x64 to 128x128 each).  Deterministic; no row-invariance
+ * contract ([TK] "Prefill kernels": chunk kernels share work across rows and are
+ * checked by agreement).
  */
 int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *stream);
 

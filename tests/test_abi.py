@@ -159,3 +159,15 @@ def test_tiles_bytes_and_pack_validation():
     g, _g = w(type_=12, m=8, k=512)
     u, _u = w(type_=12, m=8, k=512, layout=1)
     assert L.qgemv_pair_swiglu(g, u, FAKE, FAKE, 1, None) == -4   # gate and up in different layouts
+
+
+def test_prefill_shape_limits():
+    """n outside 1..2^30 and calls needing more than 2^31 - 1 tiles of Y are
+    rejected before anything reaches the device."""
+    L = qg.lib()
+    ref, _k = w(m=8)
+    assert L.qgemm_prefill(ref, FAKE, FAKE, 0, None) == -2
+    assert L.qgemm_prefill(ref, FAKE, FAKE, (1 << 30) + 1, None) == -2
+    big, _b = w(m=1 << 30)
+    assert L.qgemm_prefill(big, FAKE, FAKE, 1 << 30, None) == -2
+    assert b"tiles" in L.qg_last_error()

@@ -71,3 +71,26 @@ def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
     want = oracle.dequant64(wt, data, scales, m, k).astype(np.float16).astype(np.float32)
     want = want + np.float32(0.0)   # the sum with the zero products turns -0 into +0
     assert np.array_equal(bits(y.T.contiguous()), bits(torch.from_numpy(want)))
+
+
+def test_prefill_more_token_tiles_than_a_grid_dimension():
+    """8.4 M tokens in 128x128 tiles: 65,537 token tiles, more than a second grid
+    dimension holds; the grid is one-dimensional.  x is generated on the GPU and
+    sampled tokens (first, last, both sides of the 65,535-tile mark) are checked
+    against the oracle."""
+    import torch
+    m, k = 100, 256
+    n = 65536 * 128 + 77
+    print(f"prefill type=Q4_K m={m} k={k} n={n}", flush=True)
+    w, data, scales = weight(qg.Q4_K, m, k, 241)
+    g = torch.Generator(device=device()).manual_seed(242)
+    x = (torch.rand((n, k), generator=g, device=device(), dtype=torch.float32) * 2 - 1).to(torch.float16)
+    y = qg.qgemm_prefill(w, x)
+    torch.cuda.synchronize()
+    toks = [0, 1, 65535 * 128 - 1, 65535 * 128, 65535 * 128 + 5, n - 78, n - 1]
+    xs = x[toks].cpu().numpy()
+    got = y[toks].cpu().numpy().astype(np.float64)
+    del x, y
+    torch.cuda.empty_cache()
+    y_ref, a = oracle.gemm(qg.Q4_K, data, scales, m, k, xs)
+    assert_within(got, y_ref, a, what="prefill, 65,537 token tiles")
