@@ -138,12 +138,13 @@ def layer_call_bytes(n):
     }
 
 
-def _capture(layers, B, n, only=None):
-    """A graph of the 36-layer rotation (all four calls, or only call `only`)."""
+def _capture(layers, B, n, only=None, nsteps=LAYERS):
+    """A graph of `nsteps` layer steps over the 36-layer rotation (step i uses copy
+    i % 36): all four calls per step, or only call `only`."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(LAYERS):
+        for i in range(nsteps):
             for name, fn in layer_calls(layers[i % len(layers)], B, n):
                 if only is None or name == only:
                     fn()
@@ -151,6 +152,8 @@ def _capture(layers, B, n, only=None):
 
 
 def _time_graph(g, reps, wreps):
+    """Total ms of `reps` back-to-back replays (after `wreps` untimed), synchronized
+    on both sides."""
     import torch
     for _ in range(wreps):
         g.replay()
@@ -165,18 +168,38 @@ def _time_graph(g, reps, wreps):
     return t0.elapsed_time(t1)
 
 
-def time_layer(layers, n, steps, warmup):
-    """Time the 36-layer rotation replayed from a HIP graph, then each kernel alone.
+MIN_REPLAYS = 5
 
-    The step time comes from the graph of all four calls per layer.  Each
-    kernel's launch duration comes from a graph of that call alone over the 36
-    layers, timed with HIP events on the stream the graph runs on (HIP does not
-    allow event nodes inside a captured graph, so per-kernel events cannot sit
-    inside the step graph itself)."""
+
+def _replay_stats(g, per, reps=MIN_REPLAYS, wreps=1):
+    """Time each of `reps` replays on its own (HIP events on the stream the graph
+    runs on); `per` units of work per replay.  {median, min, max} ms per unit."""
+    import torch
+    for _ in range(wreps):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ts = sorted(ev[i].elapsed_time(ev[i + 1]) / per for i in range(reps))
+    return {"median": ts[len(ts) // 2], "min": ts[0], "max": ts[-1], "replays": reps}
+
+
+def time_layer(layers, n, steps, warmup):
+    """The contract's step timing, then statistics.
+
+    Exactly `steps` layer steps (one graph of that many steps, the copies rotating)
+    are timed between two synchronizations after `warmup` untimed steps; then the
+    same graph is replayed MIN_REPLAYS more times, each replay timed on its own, for
+    the median, minimum and maximum.  Each kernel's launch duration comes from a
+    graph of that call alone over the 36 copies, replayed MIN_REPLAYS times (HIP
+    events on the stream the graph runs on; HIP does not allow event nodes inside a
+    captured graph, so per-kernel events cannot sit inside the step graph itself)."""
     import torch
     B = Buffers(n)
-    reps = max(1, (steps + LAYERS - 1) // LAYERS)
-    wreps = max(1, (warmup + LAYERS - 1) // LAYERS)
     s = torch.cuda.Stream()   # eager warm-up on a side stream: loads code objects
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -185,15 +208,21 @@ def time_layer(layers, n, steps, warmup):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
 
-    g = _capture(layers, B, n)
-    total_ms = _time_graph(g, reps, wreps)
-    nsteps = reps * LAYERS
-    out = {"steps": nsteps, "ms_per_step": total_ms / nsteps, "graph_replays": reps}
+    if warmup > 0:
+        gw = _capture(layers, B, n, nsteps=warmup)
+        gw.replay()
+        torch.cuda.synchronize()
+        del gw
+    g = _capture(layers, B, n, nsteps=steps)
+    total_ms = _time_graph(g, 1, 0)
+    out = {"steps": steps, "ms_per_step": total_ms / steps,
+           "step_stats_ms": _replay_stats(g, steps)}
+    del g
     kus = {}
     for name in KERNELS:
         gk = _capture(layers, B, n, only=name)
-        kreps = max(1, reps // 2)
-        kus[name] = 1000.0 * _time_graph(gk, kreps, 1) / (kreps * LAYERS)
+        st = _replay_stats(gk, LAYERS)
+        kus[name] = {k: (1000.0 * v if k != "replays" else v) for k, v in st.items()}
         del gk
     out["kernel_us"] = kus
     return out
@@ -206,11 +235,11 @@ def _layer_regions(L):
             ("pair", [W["gate"].data, W["up"].data]), ("down", [W["down"].data]))
 
 
-def time_read_ceiling(layers, reps):
+def time_read_ceiling(layers):
     """The read-stream probe (plain 16-byte loads, no arithmetic) over the same
     weight bytes, in the same 36-layer rotation and call order as the layer: the
     HBM read rate this memory system gives the step's byte pattern and launch
-    count, against which the products are also reported."""
+    count, against which the products are also reported (median of the replays)."""
     import torch
     import gemm_q4_q5_amd as qg
     out = torch.zeros(qg._lib.READ_PROBE_WORDS, dtype=torch.int32, device="cuda")
@@ -225,13 +254,42 @@ def time_read_ceiling(layers, reps):
                 for name, regs in _layer_regions(layers[i % len(layers)]):
                     if only is None or name == only:
                         qg.qg_stream_read(regs, out)
-        us = 1000.0 * _time_graph(g, reps, 1) / (reps * LAYERS)
+        us = 1000.0 * _replay_stats(g, LAYERS)["median"]
         nbytes = sum(t.numel() for name, regs in _layer_regions(layers[0]) for t in regs
                      if only is None or name == only)
         res["layer" if only is None else only] = {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e3), 1),
                                                   "bytes": nbytes}
         del g
     return res
+
+
+def time_q4k_single(layers):
+    """The Q4_K GEMV alone (one matrix per call, qgemm_rows with one token = the
+    single-token kernel) on each Q4_K shape of the layer, rotated over the 36 copies,
+    at 1 and 32 tokens: median / min / max us and GB/s of the replays."""
+    import torch
+    import gemm_q4_q5_amd as qg
+    import synth
+    out = {}
+    for name in ("gate", "wq", "wo"):
+        w0 = layers[0].W[name]
+        for n in (1, 32):
+            x = torch.from_numpy(synth.activations(n, w0.k, synth.rng_for(1, 97, n))).to("cuda")
+            y = torch.empty((n, w0.m), dtype=torch.float32, device="cuda")
+            qg.qgemm_rows(w0, x, y)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(LAYERS):
+                    qg.qgemm_rows(layers[i % len(layers)].W[name], x, y)
+            st = _replay_stats(g, LAYERS)
+            b = call_bytes(12, w0.m, w0.k, n)
+            out[f"{w0.m}x{w0.k}_n{n}"] = {"us": round(1000 * st["median"], 3), "us_min": round(1000 * st["min"], 3),
+                                          "us_max": round(1000 * st["max"], 3),
+                                          "GB/s": round(b / (1e6 * st["median"]), 1),
+                                          "pct_of_peak": round(100 * b / (1e6 * st["median"]) / PEAK_HBM_GBS, 2)}
+            del g
+    return out
 
 
 LARGE_SHAPES = (("16384x8192", 16384, 8192), ("151936x2560", 151936, 2560))
@@ -335,11 +393,22 @@ def cpu_baseline(target_s=10.0):
         reps += 1
         t = time.perf_counter() - t0
     res = {"value": layer_bytes * reps / t / 1e9, "unit": "GB/s", "cores": oracle.last_threads(),
-           "kind": "oracle",
+           "kind": "oracle", "cpu_model": _cpu_model(),
            "sample": f"the full decode layer (7 projections, N=1) {reps} times, {t:.1f} s; "
                      f"oracle = plain C dequant + fp64 dot, OpenMP over rows"}
     res["extras"] = cpu_extras(mats, xs)
     return res
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _timed(fn, budget_s):
@@ -510,6 +579,7 @@ def main():
     step_bytes = sum(bytes1.values())
     ms = r1["ms_per_step"]
     value = step_bytes / (ms * 1e-3) / 1e9
+    gbs = lambda b, us: round(b / (us * 1e3), 1)
 
     res = {
         "metric": "achieved HBM GB/s (% of peak) for Q4_K GEMV, Qwen3-4B shapes, N=1 and N=32",
@@ -526,42 +596,52 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "tok_s_equiv_projections": round(1000.0 / (LAYERS * ms), 1),
     }
-    if "kernel_us" in r1:
-        ku = r1["kernel_us"]
-        res["kernels_n1"] = {k: {"us": round(ku[k], 3), "GB/s": round(bytes1[k] / (ku[k] * 1e3), 1)}
-                             for k in ku}
-        sha = kernel_source_sha()
-        pair_us = ku["pair"]
-        ach = bytes1["pair"] / (pair_us * 1e3)
-        res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                           "traffic": load_traffic(sha),
-                           "kernel": "qg::mma_kernel<1, 1, 4, 1, false, 1> (qgemv_pair, Q4_K, one token, "
-                                     f"{args.layout} layout)",
-                           "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
+    st = r1["step_stats_ms"]
+    res["step_stats"] = {"replays": st["replays"], "steps_per_replay": r1["steps"],
+                         **{f"{k}_GB/s": round(step_bytes / (st[k] * 1e-3) / 1e9, 1) for k in ("median", "min", "max")},
+                         **{f"{k}_ms_per_step": round(st[k], 5) for k in ("median", "min", "max")}}
+    ku = r1["kernel_us"]
+    res["kernels_n1"] = {k: {"us": round(v["median"], 3), "us_min": round(v["min"], 3), "us_max": round(v["max"], 3),
+                             "GB/s": gbs(bytes1[k], v["median"])} for k, v in ku.items()}
+    sha = kernel_source_sha()
+    pk = ku["pair"]
+    ach = bytes1["pair"] / (pk["median"] * 1e3)
+    res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                       "traffic": load_traffic(sha),
+                       "achieved_min": gbs(bytes1["pair"], pk["max"]), "achieved_max": gbs(bytes1["pair"], pk["min"]),
+                       "replays": pk["replays"],
+                       "kernel": f"qgemv_pair, two Q4_K 9728x2560, one token, {args.layout} layout "
+                                 "(the MFMA product kernel, one launch per call)",
+                       "algorithmic_bytes": bytes1["pair"], "kernel_source_sha": sha}
+    res["q4k_gemv"] = time_q4k_single(layers)
     if not args.no_ceiling:
-        ceil = time_read_ceiling(layers, max(1, r1["graph_replays"] // 2))
+        ceil = time_read_ceiling(layers)
         res["read_ceiling"] = ceil
         res["pct_of_read_ceiling"] = round(100.0 * value / ceil["layer"]["GB/s"] * ceil["layer"]["bytes"]
                                            / step_bytes, 2)
     if not args.no_n32:
-        r32 = time_layer(layers, 32, max(LAYERS, args.steps // 4), LAYERS)
+        r32 = time_layer(layers, 32, max(LAYERS, args.steps), LAYERS)
         b32 = layer_call_bytes(32)
         v32 = sum(b32.values()) / (r32["ms_per_step"] * 1e-3) / 1e9
+        s32 = r32["step_stats_ms"]
         res["n32"] = {"value": round(v32, 2), "unit": "GB/s", "pct_of_peak": round(100 * v32 / PEAK_HBM_GBS, 2),
-                      "ms_per_step": round(r32["ms_per_step"], 5)}
-        if "kernel_us" in r32:
-            res["n32"]["kernels"] = {k: {"us": round(v, 3), "GB/s": round(b32[k] / (v * 1e3), 1)}
-                                     for k, v in r32["kernel_us"].items()}
+                      "ms_per_step": round(r32["ms_per_step"], 5),
+                      "median_ms_per_step": round(s32["median"], 5), "min_ms_per_step": round(s32["min"], 5),
+                      "max_ms_per_step": round(s32["max"], 5),
+                      "kernels": {k: {"us": round(v["median"], 3), "us_min": round(v["min"], 3),
+                                      "us_max": round(v["max"], 3), "GB/s": gbs(b32[k], v["median"])}
+                                  for k, v in r32["kernel_us"].items()}}
     if args.layout == "tiles" and not args.no_rows:
         del layers
         torch.cuda.empty_cache()
         rows = build_layers(LAYERS, layout="rows")
         rr = time_layer(rows, 1, args.steps, args.warmup)
         res["rows_layout_n1"] = {"value": round(step_bytes / (rr["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
-                                 "ms_per_step": round(rr["ms_per_step"], 5)}
-        if "kernel_us" in rr:
-            res["rows_layout_n1"]["kernels"] = {k: round(v, 3) for k, v in rr["kernel_us"].items()}
+                                 "ms_per_step": round(rr["ms_per_step"], 5),
+                                 "median_ms_per_step": round(rr["step_stats_ms"]["median"], 5),
+                                 "kernels": {k: round(v["median"], 3) for k, v in rr["kernel_us"].items()}}
+        res["rows_layout_n1"]["q4k_gemv"] = time_q4k_single(rows)
         del rows
         torch.cuda.empty_cache()
     if not args.no_prefill:

@@ -12,15 +12,12 @@
 //   Q6_K 210 B: 128 B low nibbles, 64 B high 2-bit pairs, 16 int8 scales, fp16 d.
 //   NVFP4:      e2m1 codes (low nibble = even element), e4m3 scale per 16.
 //
-// Unpacking strategy (gfx950): quants become fp16 by OR-ing them into the
-// mantissa of a power-of-two "magic" constant, so one VALU op yields two fp16
-// lanes, and v_dot2_f32_f16 then folds two weights per instruction:
-//   low nibble  q -> fp16 1024 + q       (q in mantissa bits 0..3 (+bit 4 for Q5_K))
-//   high nibble q -> fp16 256 + 4q       (q in mantissa bits 4..7 (+bit 8 for Q5_K))
-// The bias is removed once per 32-weight sub-block with the sub-block's sum of x,
-// computed by the same dot2 chain with a (1, 1) operand, so a chain over an
-// all-zero sub-block cancels to exactly 0.  Q6_K centres q at 32; its bias
-// (1056 or 384, not powers of two) is removed the same way, per 16-weight group.
+// Unpacking (gfx950): quants become fp16 by OR-ing them into the mantissa of an
+// fp16 constant, two weights per VALU op.  The dequant probe and the prefill's fp16
+// tile use the normal-range "magic" form (low nibble q -> 1024 + q, high nibble
+// q -> 256 + 4q, recovered exactly by one subtraction); the decode product feeds the
+// quant as an fp16 subnormal (q * 2^-24 or q * 2^-20) straight into a mixed-precision
+// fma.  Q6_K centres q at 32: (1024 + q) - 1056 or (256 + 4q) - 384 per group.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,10 +38,17 @@ __device__ __forceinline__ float f16hi(uint32_t u) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
 }
 
-// dot2: c + a.x*b.x + a.y*b.y (v_dot2_f32_f16).
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+// Q4_K / Q5_K superblock: U with |w| < 2^U for every weight of the superblock, from
+// dd = d | dmin << 16 alone.  With Ed, Em the fp16 exponent fields (0 for subnormals),
+// d < 2^(Ed-14) and dmin < 2^(Em-14); sc*q <= 63*31 < 2^11 and m <= 63 < 2^6, and
+// |d*sc*q - dmin*m| <= max(d*sc*q, dmin*m).  Range -8..27.
+__device__ __forceinline__ int kq_exp_bound(uint32_t dd) {
+    const int ed = (int)((dd >> 10) & 31u), em = (int)((dd >> 26) & 31u);
+    return max(ed - 3, em - 8);
 }
+
+// Q6_K superblock: |d*sc*(q-32)| < 2^(Ed-2) (|sc| <= 128 = 2^7, |q-32| <= 32 = 2^5).
+__device__ __forceinline__ int q6_exp_bound(uint32_t dbits) { return (int)((dbits >> 10) & 31u) - 2; }
 
 // (a & m) | o in one VALU op.  VOP3 on gfx9 takes no literal operands, so the
 // compiler splits the literal-mask form into v_and + v_or; with the mask in an
@@ -91,30 +95,86 @@ __device__ __forceinline__ KqLane kq_lane_consts(int c) {
     return L;
 }
 
-// Coefficients of the lane's two sub-blocks.  For sub-block j with sum
-// S = sum (B + s*q) x  (B the magic bias, s = 1 or 4) and X = sum x, the
-// contribution is  a*(S - B*X) + b*X  with a = d*sc/s and b = -dmin*m.
-struct KqCoef {
-    float a0, b0, a1, b1;
-};
-
+// The packed 6-bit scales and mins of the lane's two sub-blocks 2c, 2c+1: sc has
+// sc_2c in bits 0..7 and sc_2c+1 in bits 8..15, mn the same for the mins.
 // hdr = the 16 header bytes: .x = d | dmin << 16, .y/.z/.w = scale bytes 0..11.
 // For sub-blocks 0..3, scale = low 6 bits of byte j, min = low 6 bits of byte j+4.
 // For 4..7: low 4 bits of both come from the nibbles of byte j+4 (scale low,
 // min high); their top 2 bits are bits 6..7 of bytes j-4 (scale) and j (min).
+__device__ __forceinline__ void kq_scale_min(uint4 hdr, const KqLane &L, uint32_t &sc, uint32_t &mn) {
+    const uint32_t t1 = __builtin_amdgcn_perm(hdr.w, hdr.y, L.sel);   // scales
+    const uint32_t t2 = __builtin_amdgcn_perm(hdr.w, hdr.z, L.sel);   // mins
+    sc = (t1 & L.mask) | ((t1 >> 18) & 0x3030u);
+    mn = ((t2 >> L.shm) & L.mask) | ((t2 >> 18) & 0x3030u);
+}
+
+// Coefficients of the lane's two sub-blocks (the dequant probe's fp32 weights): a
+// weight whose magic value is v = B + s*q (B = 1024, s = 1 for the low sub-block;
+// B = 256, s = 4 for the high one) is  a*(v - B) + b  with a = d*sc/s, b = -dmin*m.
+struct KqCoef {
+    float a0, b0, a1, b1;
+};
+
 __device__ __forceinline__ KqCoef kq_coef(uint4 hdr, const KqLane &L) {
-    uint32_t t1 = __builtin_amdgcn_perm(hdr.w, hdr.y, L.sel);   // scales
-    uint32_t t2 = __builtin_amdgcn_perm(hdr.w, hdr.z, L.sel);   // mins
-    uint32_t sc = (t1 & L.mask) | ((t1 >> 18) & 0x3030u);
-    uint32_t mn = ((t2 >> L.shm) & L.mask) | ((t2 >> 18) & 0x3030u);
-    uint32_t sm = sc | (mn << 16);
+    uint32_t sc, mn;
+    kq_scale_min(hdr, L, sc, mn);
     float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
     KqCoef k;
-    k.a0 = d * (float)(sm & 0xFFu);
-    k.a1 = (d * 0.25f) * (float)((sm >> 8) & 0xFFu);
-    k.b0 = -dmin * (float)((sm >> 16) & 0xFFu);
-    k.b1 = -dmin * (float)(sm >> 24);
+    k.a0 = d * (float)(sc & 0xFFu);
+    k.a1 = (d * 0.25f) * (float)((sc >> 8) & 0xFFu);
+    k.b0 = -dmin * (float)(mn & 0xFFu);
+    k.b1 = -dmin * (float)((mn >> 8) & 0xFFu);
     return k;
+}
+
+// 2^e as fp32 (e in -126..127).
+__device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23); }
+
+// Scaled coefficients of the lane's two sub-blocks for fp16 weight operands: with U =
+// kq_exp_bound(d | dmin << 16), a weight whose quant q sits in the mantissa of an fp16
+// subnormal (q * 2^-24 for the low sub-block, q * 2^-20 for the high one, Q5_K's fifth
+// bit included) becomes  fp16(a * v + b) = fp16((d*sc*q - dmin*m) * 2^(15-U))  in one
+// mixed-precision fma (mix2): a*v + b is exact in fp32, |result| < 2^15.
+struct KqScaled {
+    float a0, b0, a1, b1;
+    int u;
+};
+
+// u: the exponent to scale by, at least kq_exp_bound(hdr.x) (the decode product passes
+// exactly that; the prefill a running maximum over the row's superblocks, <= 27).
+__device__ __forceinline__ KqScaled kq_scaled(uint4 hdr, const KqLane &L, int u) {
+    uint32_t sc, mn;
+    kq_scale_min(hdr, L, sc, mn);
+    KqScaled k;
+    k.u = u;
+    const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
+    const float dm = -dmin * pow2f(15 - k.u);          // exact: power-of-two scaling in range
+    k.a0 = d * pow2f(39 - k.u) * (float)(sc & 0xFFu);  // <= 17 significant bits: exact
+    k.a1 = d * pow2f(35 - k.u) * (float)((sc >> 8) & 0xFFu);
+    k.b0 = dm * (float)(mn & 0xFFu);
+    k.b1 = dm * (float)((mn >> 8) & 0xFFu);
+    return k;
+}
+
+// fp16(a*v + b) for the two fp16 halves of v, one rounding each
+// (v_fma_mixlo_f16 / v_fma_mixhi_f16).
+__device__ __forceinline__ uint32_t mix2(uint32_t v, float a, float b) {
+    const h2 h = as_h2(v);
+    const _Float16 lo = (_Float16)__builtin_fmaf(a, (float)h.x, b);
+    const _Float16 hi = (_Float16)__builtin_fmaf(a, (float)h.y, b);
+    return as_u32((h2){lo, hi});
+}
+
+// The Q5_K fifth bits of four positions, OR-ed into the subnormal quant pairs of one
+// dword: hs = the fifth-bit dword shifted right by 2c (bit 0 of each byte belongs to
+// sub-block 2c, bit 1 to 2c+1), in the same byte order as the quant dword the pairs
+// came from.  lo_a/hi_a take bytes 0 and 2, lo_b/hi_b bytes 1 and 3.
+__device__ __forceinline__ void q5_fifth(uint32_t hs, uint32_t &lo_a, uint32_t &lo_b, uint32_t &hi_a,
+                                         uint32_t &hi_b) {
+    lo_a = and_or(hs << 4, 0x00100010u, lo_a);
+    lo_b = and_or(hs >> 4, 0x00100010u, lo_b);
+    hi_a = and_or(hs << 7, 0x01000100u, hi_a);
+    hi_b = and_or(hs >> 1, 0x01000100u, hi_b);
 }
 
 // Four fp16 pairs of one quant dword of a Q4_K/Q5_K chunk (positions l..l+3):
@@ -180,9 +240,8 @@ __device__ __forceinline__ float i8_at(uint32_t w, int off) {
 }
 
 // Q6_K group coefficients of lane half h: the int8 scales h, h+2 (in l0) and
-// h+4, h+6 (in l1 = the next four bytes).  For group g with dot2 sum S over its
-// magic pairs and X the same chain over x alone, the group adds
-//   a_g * (S - B_g * X),  B_g = 1056 (g < 2) or 384 (g >= 2),
+// h+4, h+6 (in l1 = the next four bytes).  A weight of group g whose magic value is
+// v (q6_oct) is  a_g * (v - B_g),  B_g = 1056 (g < 2) or 384 (g >= 2),
 //   a_g = d * sc_g (g < 2) or d * sc_g / 4 (g >= 2).
 __device__ __forceinline__ void q6_coefs(uint32_t l0, uint32_t l1, float d, int h, float (&coef)[4]) {
     const int sh = 8 * h;

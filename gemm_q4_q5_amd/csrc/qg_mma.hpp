@@ -30,16 +30,21 @@
 // pipeline is full, and a workgroup barrier after the loads, or x staged by some
 // waves for all, held whole workgroups until their slowest wave had its data.
 //
-// Exact operands.  K-quants: the weight operand is sc*q (Q4_K/Q5_K: at most
-// 63*31 = 1953, exact in fp16) and the superblock factors are applied in fp32 after
-// the MFMAs of the superblock:
-//     y += d * sum_k sc*q*x  -  dmin * sum_k m*x
-// the second sum being a second MFMA chain over the same x operands, with the
-// sub-block's min (at most 63, exact) as the weight operand.
+// Exact operands.  Q4_K/Q5_K: the weight operand is the weight itself, rounded once
+// to fp16 at a power-of-two scale of its (row, superblock):
+//     w' = fp16((d*sc*q - dmin*m) * 2^(15-U)),   y += 2^(U-15) * sum_k w'*x
+// with U = max(Ed - 3, Em - 8) from the fp16 exponent fields Ed, Em of d and dmin, so
+// |w| < 2^U and |w'| < 2^15 (no overflow), and every weight of magnitude at least
+// 2^(U-29) is an fp16 normal (relative error <= 2^-11 of |w| itself).  A weight that
+// is exactly zero stays exactly zero, and the error of a row scales with
+// sum|w||x|, not with the sizes of the two terms that cancel in it.  The quant
+// enters the mixed-precision fma as an fp16 subnormal (its bits in the low mantissa),
+// so a*q + b is formed exactly in fp32 and rounded once.
 // Q6_K: the operand is sc*(q-32), exact whenever |sc*(q-32)| <= 2048 (every
 // |sc| <= 64, which covers int8 scales drawn in 0..63), otherwise rounded once to
 // fp16 (relative error <= 2^-11); d is applied in fp32.  NVFP4: e2m1 * e4m3 is exact
-// in fp16 and the MFMA accumulates over all of K.
+// in fp16 and the MFMA accumulates over all of K.  FP8: the code is exact in fp16
+// and the bf16 block scale is applied in fp32 per 128-wide block.
 //
 // Row invariance.  An output (t, r) is produced by the same instructions for every
 // n: its MFMAs see only token t's x (A row t) and row r's weights (B column r);
@@ -171,10 +176,6 @@ __device__ __forceinline__ h2 h2c(float v) {
     const _Float16 h = (_Float16)v;
     return (h2){h, h};
 }
-// Fused a*b + c on fp16 pairs (one rounding: v_pk_fma_f16).
-__device__ __forceinline__ uint32_t pk_fma(uint32_t a, h2 b, h2 c) {
-    return as_u32(__builtin_elementwise_fma(as_h2(a), b, c));
-}
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, h2 b) { return as_u32(as_h2(a) * b); }
 
 __device__ __forceinline__ h8 mk_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -296,56 +297,31 @@ __device__ __forceinline__ void xhalf_commit(int q, bool st, const XHalf &X, uin
 }
 
 // ---------------------------------------------------------------------------
-// Q4_K / Q5_K weight operand of step s.  Quant dword s of the lane's chunk (bytes
-// 4s..4s+3 = positions 4s..4s+3 of sub-blocks 2g (low nibbles) and 2g+1 (high)):
-//   lo02 = 1024 + q at (4s, 4s+2), lo13 at (4s+1, 4s+3)     [fp16 magic, exact]
-//   hi02 = 256 + 4q at (32+4s, 34+4s), hi13 at (33+4s, 35+4s)
-// sc*q = (1024+q)*sc - 1024*sc = (256+4q)*(sc/4) - 64*sc with one fused rounding
-// of an exactly representable value.
-struct KqTile {
-    h2 S0, B0, S1, B1;
-    h8 bm;           // min operand: m_2g on the low-sub-block slots, m_2g+1 on the high ones
-    float d, dmin;
-};
+// Q4_K / Q5_K weight operand of step s.  Quant dword s of the lane's chunk holds
+// positions 4s..4s+3 of sub-block 2g (low nibbles) and of sub-block 2g+1 (high
+// nibbles).  Masked in place, each 16-bit half is an fp16 subnormal carrying the
+// quant in its mantissa: q * 2^-24 (low nibble, bits 0..3, Q5_K's fifth bit at 4) or
+// q * 2^-20 (high nibble, bits 4..7, fifth bit at 8); the sub-block's coefficients
+// absorb the 2^24 / 2^20, so one mixed-precision fma per weight gives
+//     w' = fp16(a*q + b),   a = d*sc*2^(15-U),  b = -dmin*m*2^(15-U)
+// with a*q + b exact in fp32 before its one rounding.  Slot order of the step:
+//     (4s, 4s+2), (4s+1, 4s+3) of sub-block 2g, then the same of 2g+1.
+typedef KqScaled KqTile;   // a0 carries 2^24, a1 2^20 (the quants' subnormal scales)
 
-__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, int g) {
-    const KqLane L = kq_lane_consts(g);
-    const uint32_t t1 = __builtin_amdgcn_perm(R.hdr.w, R.hdr.y, L.sel);
-    const uint32_t t2 = __builtin_amdgcn_perm(R.hdr.w, R.hdr.z, L.sel);
-    const uint32_t sc = (t1 & L.mask) | ((t1 >> 18) & 0x3030u);
-    const uint32_t mn = ((t2 >> L.shm) & L.mask) | ((t2 >> 18) & 0x3030u);
-    const float sc0 = (float)(sc & 0xFFu), sc1 = (float)((sc >> 8) & 0xFFu);
-    KqTile k;
-    k.S0 = h2c(sc0);
-    k.B0 = h2c(-1024.0f * sc0);
-    k.S1 = h2c(0.25f * sc1);
-    k.B1 = h2c(-64.0f * sc1);
-    const uint32_t m0 = as_u32(h2c((float)(mn & 0xFFu))), m1 = as_u32(h2c((float)((mn >> 8) & 0xFFu)));
-    k.bm = mk_h8(m0, m0, m1, m1);
-    k.d = f16lo(R.hdr.x);
-    k.dmin = f16hi(R.hdr.x);
-    return k;
-}
+__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, int g) { return kq_scaled(R.hdr, kq_lane_consts(g), kq_exp_bound(R.hdr.x)); }
 
 template <bool Q5>
 __device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, int s) {
     const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
     const uint32_t w = qw[s], w8 = w >> 8;
-    uint32_t lo02 = and_or(w, 0x000F000Fu, 0x64006400u);
-    uint32_t lo13 = and_or(w8, 0x000F000Fu, 0x64006400u);
-    uint32_t hi02 = and_or(w, 0x00F000F0u, 0x5C005C00u);
-    uint32_t hi13 = and_or(w8, 0x00F000F0u, 0x5C005C00u);
+    uint32_t lo02 = w & 0x000F000Fu, lo13 = w8 & 0x000F000Fu;
+    uint32_t hi02 = w & 0x00F000F0u, hi13 = w8 & 0x00F000F0u;
     if (Q5) {
         // fifth bits: bit 2g (low sub-block) and 2g+1 (high) of qh byte l
         const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
-        const uint32_t hs = hw[s] >> (2 * g);
-        lo02 = and_or(hs << 4, 0x00100010u, lo02);
-        lo13 = and_or(hs >> 4, 0x00100010u, lo13);
-        hi02 = and_or(hs << 7, 0x01000100u, hi02);
-        hi13 = and_or(hs >> 1, 0x01000100u, hi13);
+        q5_fifth(hw[s] >> (2 * g), lo02, lo13, hi02, hi13);
     }
-    return mk_h8(pk_fma(lo02, K.S0, K.B0), pk_fma(lo13, K.S0, K.B0), pk_fma(hi02, K.S1, K.B1),
-                 pk_fma(hi13, K.S1, K.B1));
+    return mk_h8(mix2(lo02, K.a0, K.b0), mix2(lo13, K.a0, K.b0), mix2(hi02, K.a1, K.b1), mix2(hi13, K.a1, K.b1));
 }
 
 // Q6_K.  Lane chunk g = half h6 = g >> 1, quarter q6 = g & 1 (positions 16*q6 ..
@@ -444,31 +420,23 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
                                     f4 (&acc)[NT][NG]) {
     const uint4 *const(&xv)[NG] = xa;   // LDS reads at their use; other waves hide the latency
     if constexpr (T == T_Q4_K || T == T_Q5_K) {
-        // c1 = sum_k sc*q*x and c2 = sum_k m*x over the superblock (m of the
-        // position's sub-block), both from the same x operands; y += d*c1 - dmin*c2.
+        // c = sum_k w'*x over the superblock (one MFMA chain); y += 2^(U-15) * c.
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             const KqTile K = kq_tile(R[i], g);
-            f4 c1[NG], c2[NG];
+            f4 c1[NG];
 #pragma unroll
-            for (int q = 0; q < NG; ++q) c1[q] = c2[q] = (f4){0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const h8 b = kq_step<T == T_Q5_K>(R[i], K, g, s);
 #pragma unroll
-                for (int q = 0; q < NG; ++q) {
-                    const h8 a = u4h8(xv[q][s]);
-                    c1[q] = mfma(a, b, c1[q]);
-                    c2[q] = mfma(a, K.bm, c2[q]);
-                }
+                for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
             }
 #pragma unroll
             for (int q = 0; q < NG; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v = __builtin_fmaf(K.d, c1[q][e], acc[i][q][e]);
-                    acc[i][q][e] = __builtin_fmaf(-K.dmin, c2[q][e], v);
-                }
+                for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(pow2f(K.u - 15), c1[q][e], acc[i][q][e]);
         }
     } else if constexpr (T == T_Q6_K) {
 #pragma unroll
@@ -707,8 +675,9 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     const int KS = S.ks, KW = KS / NP, lkw = __builtin_ctz((unsigned)KW), tpw = WV >> lkw;
     const int kw = wave & (KW - 1), rt = wave >> lkw;
     // Ring depth: three superblocks with one phase per wave; with several, four (two
-    // in 16-wave workgroups, which have 128 registers).
-    constexpr int D = NP == 1 ? kDepth : (WV <= 8 ? 4 : 2);
+    // in 16-wave workgroups, which have 128 registers, and one there with four phases
+    // of two token groups, whose accumulators alone take 32 of them).
+    constexpr int D = NP == 1 ? kDepth : (WV <= 8 ? 4 : (NP == 4 && NG == 2 ? 1 : 2));
     const int j = lane & 15, g = lane >> 4;
     const int up = SW ? (rt & 1) : 0;   // SwiGLU: 0 for a gate tile group, 1 for an up one
     const int64_t unit = SW ? (int64_t)(bid - S.wg_begin) * (tpw >> 1) + (rt >> 1)

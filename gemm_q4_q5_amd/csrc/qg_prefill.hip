@@ -6,9 +6,16 @@
 // whose dequantized weight tile is shared by every wave of the block (E5).  Here
 // a workgroup of four waves owns a BM x BN tile of Y (tokens x weight rows) and
 // walks K in 128-wide steps through LDS: X[BM][128] as stored (fp16) and the
-// dequantized W[BN][128] (fp16: the exact weight rounded once, to nearest even;
-// |error| <= 2^-11 |w|); each wave runs v_mfma_f32_16x16x32_f16 over its
+// dequantized W[BN][128]; each wave runs v_mfma_f32_16x16x32_f16 over its
 // (BM/2) x (BN/2) sub-tile with fp32 accumulation.
+//
+// The W tile is fp16: each weight scaled by a power of two 2^(15-U) of its row, then
+// rounded once to nearest even.  U bounds the magnitudes of the row's weights (|w| <
+// 2^U; the largest of its superblocks' bounds, read from their d / dmin, or from
+// FP8's block scales, before the K loop), so the scaled weight never overflows fp16,
+// and a weight no smaller than 2^(U-29) is an fp16 normal (|error| <= 2^-11 |w|); an
+// exactly zero weight stays zero.  The row's sums are scaled back (exactly) when
+// stored.  NVFP4 weights are exact in fp16 and need no scale.
 //
 // With two LDS tile pairs (the 128x64 and 64x64 tiles) the steps are pipelined
 // with one barrier each: while step s's MFMAs drain, step s+1's X (loaded into
@@ -50,36 +57,32 @@ __device__ __forceinline__ typename Loader<T>::Raw p_load(const PrefillArgs &A, 
     return Loader<T>::load(A.data, A.scales, A.row_bytes, r, b, c, A.tiled);
 }
 
-// Write the task's 64 weights (fp16, one rounding of the exact fp32 value) into
-// row `row` of the LDS weight tile, at their K offsets within the step (in 16-byte
-// chunks, swizzled).
+// Write the task's 64 weights into row `row` of the LDS weight tile (fp16, the exact
+// weight times 2^(15-u) rounded once; u = the row's bound, p_row_exp), at their K
+// offsets within the step (in 16-byte chunks, swizzled).
 template <int T>
-__device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt, int hf, uint4 *tile, int row) {
+__device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt, int hf, uint4 *tile, int row,
+                                        int u) {
     const int c = 2 * (kt & 1) + hf;
     if (T == T_Q4_K || T == T_Q5_K) {
-        // chunk c: sub-block 2c at step offsets 64hf + 0..31, 2c+1 at 64hf + 32..63
+        // chunk c: sub-block 2c at step offsets 64hf + 0..31, 2c+1 at 64hf + 32..63.
+        // Byte-paired quant dwords give positions (l, l+1) and (l+2, l+3) in the 16-bit
+        // halves, each quant an fp16 subnormal (kq_scaled), one mixed fma per weight.
         const RawKq &Q = reinterpret_cast<const RawKq &>(R);
-        const KqCoef cf = kq_coef(Q.hdr, kq_lane_consts(c));
-        // w = a*q + b with the exact products a = d*sc, b = -dmin*m: q is recovered
-        // exactly from the fp16 magic value (v - 1024, v - 256 = 4q).  The fma and
-        // the fp16 conversion compile to one mixed-precision fma with an fp16 result
-        // (v_fma_mix{lo,hi}_f16), which rounds the exact a*q + b once, straight to
-        // fp16; an fp32 result rounded again to fp16 would differ where the fp32
-        // value lands on an fp16 tie.
+        const KqScaled cf = kq_scaled(Q.hdr, kq_lane_consts(c), u);
         const uint32_t qw[8] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w};
         const uint32_t hw[8] = {Q.h0.x, Q.h0.y, Q.h0.z, Q.h0.w, Q.h1.x, Q.h1.y, Q.h1.z, Q.h1.w};
-        const h2 m0 = {(_Float16)1024.0f, (_Float16)1024.0f}, m1 = {(_Float16)256.0f, (_Float16)256.0f};
         uint32_t lo[16], hi[16];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const Quad qd = T == T_Q5_K ? q5_quad(qw[i], pair_bytes(hw[i], hw[i], kSelAligned) >> (2 * c))
-                                        : q4_quad(qw[i]);
-            const h2 p0 = as_h2(qd.lo01) - m0, p1 = as_h2(qd.lo23) - m0;   // exact small integers
-            const h2 p2 = as_h2(qd.hi01) - m1, p3 = as_h2(qd.hi23) - m1;
-            lo[2 * i] = pack_h2(__builtin_fmaf(cf.a0, (float)p0.x, cf.b0), __builtin_fmaf(cf.a0, (float)p0.y, cf.b0));
-            lo[2 * i + 1] = pack_h2(__builtin_fmaf(cf.a0, (float)p1.x, cf.b0), __builtin_fmaf(cf.a0, (float)p1.y, cf.b0));
-            hi[2 * i] = pack_h2(__builtin_fmaf(cf.a1, (float)p2.x, cf.b1), __builtin_fmaf(cf.a1, (float)p2.y, cf.b1));
-            hi[2 * i + 1] = pack_h2(__builtin_fmaf(cf.a1, (float)p3.x, cf.b1), __builtin_fmaf(cf.a1, (float)p3.y, cf.b1));
+            const uint32_t p = pair_bytes(qw[i], qw[i], kSelAligned), p8 = p >> 8;
+            uint32_t l01 = p & 0x000F000Fu, l23 = p8 & 0x000F000Fu;
+            uint32_t h01 = p & 0x00F000F0u, h23 = p8 & 0x00F000F0u;
+            if (T == T_Q5_K) q5_fifth(pair_bytes(hw[i], hw[i], kSelAligned) >> (2 * c), l01, l23, h01, h23);
+            lo[2 * i] = mix2(l01, cf.a0, cf.b0);
+            lo[2 * i + 1] = mix2(l23, cf.a0, cf.b0);
+            hi[2 * i] = mix2(h01, cf.a1, cf.b1);
+            hi[2 * i + 1] = mix2(h23, cf.a1, cf.b1);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -96,7 +99,7 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
         const uint32_t l0 = __builtin_amdgcn_alignbyte(Q.s01.y, Q.s01.x, Q.mis);
         const uint32_t l1 = __builtin_amdgcn_alignbyte(Q.s2, Q.s01.y, Q.mis);
         float coef[4];
-        q6_coefs(l0, l1, f16lo(Q.d), hf, coef);
+        q6_coefs(l0, l1, f16lo(Q.d) * pow2f(15 - u), hf, coef);   // d scaled: exact
         uint32_t out[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -104,7 +107,7 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
                                    pair_bytes(hv[i + 1], hv[i], sel));
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float nb = (g < 2 ? -1056.0f : -384.0f) * coef[g];   // exact: coef has <= 19 bits
+                const float nb = (g < 2 ? -1056.0f : -384.0f) * coef[g];   // exact: coef has <= 18 bits
 #pragma unroll
                 for (int e = 0; e < 2; ++e)
                     out[g][2 * i + e] = pack_h2(__builtin_fmaf(coef[g], f16lo(o.v[g][e]), nb),
@@ -117,10 +120,11 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
             tile[swz(row, 4 * g + 2 * hf + 1)] = make_uint4(out[g][4], out[g][5], out[g][6], out[g][7]);
         }
     } else if (T == T_FP8) {
-        // FP8 chunk c: 64 codes at step offsets 64hf + 0..63; code * scale is exact in
-        // fp32 (4 + 8 significant bits) and rounded once to fp16.
+        // FP8 chunk c: 64 codes at step offsets 64hf + 0..63, all in one 128-wide scale
+        // block.  s * 2^(15-u) is exact in fp32 and code * (s * 2^(15-u)) has at most
+        // 4 + 8 significant bits: rounded once to fp16.
         const RawF8 &Q = reinterpret_cast<const RawF8 &>(R);
-        const float sc = bf16_lo(Q.sc);
+        const float sc = bf16_lo(Q.sc) * pow2f(15 - u);
         const uint32_t qw[16] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w,
                                  Q.q2.x, Q.q2.y, Q.q2.z, Q.q2.w, Q.q3.x, Q.q3.y, Q.q3.z, Q.q3.w};
 #pragma unroll
@@ -130,7 +134,7 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
                               pack_h2(e4m3_at(b, 0) * sc, e4m3_at(b, 1) * sc), pack_h2(e4m3_at(b, 2) * sc, e4m3_at(b, 3) * sc));
         }
     } else {
-        // NVFP4 chunk c: 64 codes at step offsets 64hf + 0..63, four scales
+        // NVFP4 chunk c: 64 codes at step offsets 64hf + 0..63, four scales (exact, U = 15)
         const RawF4 &Q = reinterpret_cast<const RawF4 &>(R);
         const uint32_t qw[8] = {Q.q0.x, Q.q0.y, Q.q0.z, Q.q0.w, Q.q1.x, Q.q1.y, Q.q1.z, Q.q1.w};
 #pragma unroll
@@ -144,6 +148,37 @@ __device__ __forceinline__ void p_store(const typename Loader<T>::Raw &R, int kt
     }
 }
 
+// Whether the tile's weights are scaled (every type but NVFP4).
+template <int T>
+constexpr bool p_scaled() { return T != T_NVFP4; }
+
+// U of weight row r: |w| < 2^U for every weight of the row.  K-quants: the largest
+// superblock bound (kq_exp_bound, q6_exp_bound); FP8: |code| <= 448 < 2^9 and a bf16
+// scale with exponent field Es is below 2^(Es-126), so |w| < 2^(Es-117), clamped at
+// -110 (the tiniest scales) so that 2^(15-U) stays an fp32 normal.  Reads only the
+// d / dmin / scale fields, which the K loop reads again from cache.
+template <int T>
+__device__ __forceinline__ int p_row_exp(const PrefillArgs &A, int64_t r) {
+    int u = -1000;
+    const int nb = A.k / 256;
+    if constexpr (T == T_Q4_K || T == T_Q5_K || T == T_Q6_K) {
+        const int S = T == T_Q4_K ? 144 : (T == T_Q5_K ? 176 : 210);
+#pragma unroll 8
+        for (int b = 0; b < nb; ++b) {
+            const uint8_t *blk = kq_block(A.data, A.row_bytes, S, r, b, A.tiled);
+            if constexpr (T == T_Q6_K) u = max(u, q6_exp_bound(*reinterpret_cast<const uint16_t *>(blk + 208)));
+            else u = max(u, kq_exp_bound(*reinterpret_cast<const uint32_t *>(blk)));
+        }
+    } else if constexpr (T == T_FP8) {
+        const uint16_t *srow = reinterpret_cast<const uint16_t *>(A.scales + (r >> 7) * (A.row_bytes / 64));
+#pragma unroll 8
+        for (int b = 0; b < 2 * nb; ++b) u = max(u, max((int)((srow[b] >> 7) & 0xFFu) - 117, -110));
+    } else {
+        u = 15;
+    }
+    return u;
+}
+
 // DB: double-buffered tiles, one barrier per step (see the header); otherwise one
 // tile pair and two barriers per step: write step s's X and weights, barrier,
 // issue step s+1's loads, MFMAs, barrier.  The 128x128 tile keeps the single buffer:
@@ -154,9 +189,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
     constexpr int TM = BM / 32, TN = BN / 32;   // 16x16 MFMA tiles per wave (2 x 2 waves)
     constexpr int XC = BM * 16, WC = BN * 16;   // 16-byte chunks per X / W stage
     constexpr int XL = XC / 256;                // 16-byte X loads per thread per step
-    extern __shared__ uint4 lds[];              // X stage(s), then W stage(s)
+    extern __shared__ uint4 lds[];              // X stage(s), W stage(s), then the rows' U per W stage
     uint4 *const xst = lds;
     uint4 *const wst = lds + (DB ? 2 : 1) * XC;
+    int *const su = reinterpret_cast<int *>(wst + (DB ? 2 : 1) * WC);   // [BN]: the rows' U
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -201,6 +237,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
         for (int j = 0; j < TN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
 
     const int arow = wm * (BM / 2) + (lane & 15), brow = wn * (BN / 2) + (lane & 15);
+    // The dequant thread's row exponent; the MFMA lanes read their rows' from LDS at
+    // the end (su is written before the loop's first barrier).
+    const int urow = dq ? p_row_exp<T>(A, wr) : 15;
+    if (dq && dhf == 0) su[drow] = urow;
     if constexpr (!DB) {
         typename Loader<T>::Raw raw;
         u32x4 xv[XL];
@@ -209,7 +249,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
         for (int s = 0; s < nk; ++s) {
             __syncthreads();   // the previous step's readers are done
             store_x(xv, 0);
-            if (dq) p_store<T>(raw, s, dhf, wst, drow);
+            if (dq) p_store<T>(raw, s, dhf, wst, drow, urow);
             __syncthreads();
             if (s + 1 < nk) {   // in flight during this step's MFMAs
                 load_x(xv, s + 1);
@@ -239,7 +279,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
         load_x(xv, 0);
         store_x(xv, 0);
         if (dq) {
-            p_store<T>(raw, 0, dhf, wst, drow);
+            p_store<T>(raw, 0, dhf, wst, drow, urow);
             raw = p_load<T>(A, wr, 1, dhf);
         }
         load_x(xv, 1);
@@ -278,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
             store_x(xv, p ^ 1);
             load_x(xv, s2);
             if (dq) {
-                p_store<T>(raw, s1, dhf, wst + (p ^ 1) * WC, drow);
+                p_store<T>(raw, s1, dhf, wst + (p ^ 1) * WC, drow, urow);
                 raw = p_load<T>(A, wr, s2, dhf);
             }
         }
@@ -289,10 +329,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs A) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int64_t r = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
+            const float back = p_scaled<T>() ? pow2f(su[wn * (BN / 2) + 16 * j + (lane & 15)] - 15) : 1.0f;   // exact
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t t = m0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + e;
-                if (t < A.n && r < A.m) A.y[t * A.m + r] = acc[i][j][e];
+                if (t < A.n && r < A.m) A.y[t * A.m + r] = acc[i][j][e] * back;
             }
         }
 }
@@ -302,7 +343,7 @@ static hipError_t launch_tile(const PrefillArgs &A, hipStream_t st) {
     const int64_t blocks = (A.m + BN - 1) / BN * ((A.n + BM - 1) / BM);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
-    const size_t lds = (size_t)(BM + BN) * 256 * (DB ? 2 : 1);
+    const size_t lds = (size_t)(BM + BN) * 256 * (DB ? 2 : 1) + (size_t)BN * 4;
     const void *fn = (const void *)prefill_kernel<T, BM, BN, DB>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

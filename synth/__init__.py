@@ -161,3 +161,147 @@ QWEN3_4B_LAYER = (
     ("up", Q4_K, 9728, 2560),
     ("down", Q6_K, 2560, 9728),
 )
+
+
+# ---------------------------------------------------------------------------
+# Adversarial K-quant rows: weights d*sc*q - dmin*m whose two terms cancel.
+#
+# These are built from integer relations between the stored fields (no weight is
+# decoded here).  With d = D * 2^e and dmin = Dm * 2^(e + j) (D, Dm the 11-bit fp16
+# significands), a sub-block whose 32 quants all equal q has every weight equal to
+# 2^e * (D*sc*q - Dm*m*2^j).
+#   * "exact": D*sc*q == Dm*m*2^j, every weight exactly 0 (sum|w||x| = 0);
+#   * "near":  D*sc*q - Dm*m*2^j = +-1 with D*sc*q >= 10^6, so 0 < |w| <= 1e-6 * d*sc*q;
+#   * "mixed": per superblock, sub-blocks of both kinds beside ordinary small ones
+#     (sc = 1, m = 0, random quants), so sum|w||x| is small next to the cancelling terms.
+
+
+def _pack_scale_min(sc, mn):
+    """The 12 packed bytes of eight 6-bit (scale, min) pairs, GGML K-quant packing:
+    pairs 0..3 in the low 6 bits of bytes j (scale) and j+4 (min); pairs 4..7 with
+    their low 4 bits in byte j+4 (scale low nibble, min high nibble) and their top 2
+    bits in bits 6..7 of bytes j-4 (scale) and j (min)."""
+    sc = np.asarray(sc, dtype=np.int64)
+    mn = np.asarray(mn, dtype=np.int64)
+    out = np.zeros(sc.shape[:-1] + (12,), dtype=np.int64)
+    for j in range(4):
+        out[..., j] = sc[..., j] | ((sc[..., j + 4] >> 4) << 6)
+        out[..., j + 4] = mn[..., j] | ((mn[..., j + 4] >> 4) << 6)
+        out[..., j + 8] = (sc[..., j + 4] & 15) | ((mn[..., j + 4] & 15) << 4)
+    return out.astype(np.uint8)
+
+
+def _fp16_from_parts(sig, e):
+    """fp16 bits of sig * 2^e for an 11-bit significand sig in [1024, 2047] (normal)."""
+    sig = np.asarray(sig, dtype=np.int64)
+    e = np.asarray(e, dtype=np.int64)
+    field = e + 10 + 15
+    assert np.all((sig >= 1024) & (sig < 2048)) and np.all((field >= 1) & (field <= 30))
+    return ((field << 10) | (sig - 1024)).astype(np.uint16)
+
+
+def _exact_triples(R, qmax):
+    """(sc, q, m) with sc*q == R*m, 1 <= sc, m <= 63, 1 <= q <= qmax."""
+    out = []
+    for sc in range(1, 64):
+        for q in range(1, qmax + 1):
+            if (sc * q) % R == 0 and 1 <= (sc * q) // R <= 63:
+                out.append((sc, q, (sc * q) // R))
+    return out
+
+
+_NEAR_POOLS = {}
+
+
+def _near_pool(qmax):
+    """Every (D, Dm, j) -> [(sc, q, m)] with D*sc*q - Dm*m*2^j = +-1 and D*sc*q >= 10^6
+    (D odd in [1025, 2047], Dm in [1024, 2047], j in 3..5, sc, m in 1..63, q in 1..qmax),
+    found once by exhaustive search."""
+    if qmax in _NEAR_POOLS:
+        return _NEAR_POOLS[qmax]
+    sc = np.arange(1, 64, 2)[:, None, None]          # D*sc*q must be odd
+    q = np.arange(1, qmax + 1, 2)[None, :, None]
+    mm = np.arange(1, 64)[None, None, :]
+    pool = {}
+    for j in (3, 4, 5):
+        for D in range(1025, 2048, 2):
+            P = D * sc * q
+            for delta in (-1, 1):
+                num = P - delta
+                den = mm * (1 << j)
+                Dm = num // den
+                ok = (num % den == 0) & (Dm >= 1024) & (Dm < 2048) & (P >= 10 ** 6)
+                for a, b, c in zip(*np.nonzero(ok)):
+                    key = (D, int(Dm[a, b, c]), j)
+                    pool.setdefault(key, []).append((int(sc[a, 0, 0]), int(q[0, b, 0]), int(mm[0, 0, c])))
+    keys = sorted(pool)
+    _NEAR_POOLS[qmax] = (keys, pool)
+    return _NEAR_POOLS[qmax]
+
+
+def kquant_cancelling(wtype: int, m: int, k: int, rng: np.random.Generator, mode: str = "exact"):
+    """Q4_K / Q5_K rows of cancelling superblocks (see above), as raw bytes [m, row_bytes],
+    plus the fields they were built from: a dict of arrays d, dmin (fp16 bits, [m, nb]),
+    sc, mn, q ([m, nb, 8]: every quant of sub-block j is q[..., j])."""
+    if wtype not in (Q4_K, Q5_K):
+        raise ValueError("cancellation needs the Q4_K / Q5_K affine")
+    if mode not in ("exact", "near", "mixed"):
+        raise ValueError(mode)
+    qmax = 15 if wtype == Q4_K else 31
+    nb = k // QK
+    d_bits = np.zeros((m, nb), np.uint16)
+    dm_bits = np.zeros((m, nb), np.uint16)
+    sc = np.zeros((m, nb, 8), np.int64)
+    mn = np.zeros((m, nb, 8), np.int64)
+    qv = np.zeros((m, nb, 8), np.int64)
+    exact_pool = {R: _exact_triples(R, qmax) for R in range(1, 64)}
+    for r in range(m):
+        for b in range(nb):
+            kind = mode if mode != "mixed" else ("exact", "near")[int(rng.integers(0, 2))]
+            if kind == "exact":
+                if rng.integers(0, 2):   # d a power of two, dmin = R * d (R <= 63 fits 11 bits)
+                    e = int(rng.integers(-10, -6))
+                    R = int(rng.integers(2, 64))
+                    while not exact_pool[R]:
+                        R = int(rng.integers(2, 64))
+                    D, De, Dm, Dme = 1024, e - 10, R, e   # d = 2^e = 1024 * 2^(e-10), dmin = R * 2^e
+                    while Dm < 1024:
+                        Dm, Dme = Dm * 2, Dme - 1
+                    trip = exact_pool[R]
+                else:                    # any d, dmin = 2^r * d
+                    D, De = int(rng.integers(1024, 2048)), int(rng.integers(-20, -16))
+                    r_ = int(rng.integers(0, 4))
+                    Dm, Dme = D, De + r_
+                    trip = exact_pool[1 << r_]
+            else:
+                keys, pool = _near_pool(qmax)
+                D, Dm, j = keys[int(rng.integers(0, len(keys)))]
+                trip = pool[(D, Dm, j)]
+                De = int(rng.integers(-20, -18))
+                Dme = De + j
+            d_bits[r, b] = _fp16_from_parts(D, De)
+            dm_bits[r, b] = _fp16_from_parts(Dm, Dme)
+            picks = rng.integers(0, len(trip), size=8)
+            for s in range(8):
+                sc[r, b, s], qv[r, b, s], mn[r, b, s] = trip[picks[s]]
+            if mode == "mixed":          # ordinary small sub-blocks beside the cancelling ones
+                for s in np.nonzero(rng.integers(0, 3, size=8) == 0)[0]:
+                    sc[r, b, s], mn[r, b, s], qv[r, b, s] = 1, 0, -1   # -1: random quants
+    bb = BLOCK_BYTES[wtype]
+    blocks = np.zeros((m, nb, bb), np.uint8)
+    _put_u16(blocks, 0, d_bits)
+    _put_u16(blocks, 2, dm_bits)
+    blocks[..., 4:16] = _pack_scale_min(sc, mn)
+    qoff = 16 if wtype == Q4_K else 48
+    rnd = rng.integers(0, qmax + 1, size=(m, nb, 8, 32))
+    quants = np.where(qv[..., None] >= 0, qv[..., None], rnd)         # [m, nb, 8 sub-blocks, 32]
+    for c in range(4):   # chunk c: sub-block 2c in the low nibbles, 2c+1 in the high ones
+        lo, hi = quants[:, :, 2 * c] & 15, quants[:, :, 2 * c + 1] & 15
+        blocks[..., qoff + 32 * c:qoff + 32 * c + 32] = (lo | (hi << 4)).astype(np.uint8)
+    if wtype == Q5_K:    # fifth bit of position l of sub-block j: bit j of qh[l]
+        qh = np.zeros((m, nb, 32), np.int64)
+        for s in range(8):
+            qh |= ((quants[:, :, s] >> 4) & 1) << s
+        blocks[..., 16:48] = qh.astype(np.uint8)
+    fields = {"d": d_bits, "dmin": dm_bits, "sc": sc, "mn": mn, "q": quants}
+    return blocks.reshape(m, nb * bb), fields

@@ -1,11 +1,11 @@
 """GPU parity of the MFMA prefill GEMM against the CPU oracle.
 
-The weight operand is the exact weight rounded once to fp16 (round to nearest
-even), so the output is held to |y - y_ref| <= 2e-3 * sum|w||x| against the
-oracle's fp64 product, and -- much tighter -- to fp32-accumulation error against
-the fp64 product of the oracle's exact weights rounded to fp16 (which pins the
-MFMA operand layout).  An identity input returns the operand itself, compared
-bit for bit.
+The weight operand is the exact weight times a power of two of its row, rounded
+once to fp16 (round to nearest even), so the output is held to |y - y_ref| <=
+2e-3 * sum|w||x| against the oracle's fp64 product, and -- much tighter -- to
+fp32-accumulation error against the fp64 product of the oracle's exact weights
+rounded that way (which pins the MFMA operand layout).  An identity input returns
+the operand itself, compared bit for bit.
 """
 import numpy as np
 import pytest
@@ -13,7 +13,7 @@ import pytest
 import gemm_q4_q5_amd as qg
 import oracle
 import synth
-from gpu_util import assert_within, bits, device, weight, x_dev
+from gpu_util import assert_within, bits, device, prefill_operand, weight, x_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def test_prefill_vs_oracle(wt, m, k, n):
     y_ref, a = oracle.gemm(wt, data, scales, m, k, x)
     assert_within(got, y_ref, a, what=f"prefill type {wt}")
     # fp64 product of the fp16-rounded weights: only fp32 accumulation error remains
-    w16 = oracle.dequant64(wt, data, scales, m, k).astype(np.float16).astype(np.float64)
+    w16 = prefill_operand(wt, data, scales, m, k)
     y16 = x.astype(np.float64) @ w16.T
     a16 = np.abs(x.astype(np.float64)) @ np.abs(w16).T
     assert_within(got, y16, a16, tol=2e-6, what=f"prefill type {wt} vs fp16 weights")
@@ -60,15 +60,16 @@ def test_prefill_deterministic():
 @pytest.mark.parametrize("m,k", [(300, 512), (1500, 2048), (1250, 1280), (2048, 2048)])
 def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
     """x = I (k tokens): y[t][r] is the kernel's fp16 operand for w[r][t] (one
-    nonzero product, exact in fp32), which must equal the oracle's exact weight
-    rounded once to fp16 -- not the fp32 weight rounded again, which differs where
-    the fp32 value lands on an fp16 tie."""
+    nonzero product, exact in fp32) scaled back by its row's power of two, which must
+    equal the oracle's exact weight scaled by it and rounded once to fp16 -- not the
+    fp32 weight rounded again, which differs where the fp32 value lands on an fp16
+    tie."""
     import torch
     print(f"prefill operand type={wt} m={m} k={k}", flush=True)
     w, data, scales = weight(wt, m, k, 231)
     y = qg.qgemm_prefill(w, x_dev(np.eye(k, dtype=np.float16)))
     torch.cuda.synchronize()
-    want = oracle.dequant64(wt, data, scales, m, k).astype(np.float16).astype(np.float32)
+    want = prefill_operand(wt, data, scales, m, k).astype(np.float32)
     want = want + np.float32(0.0)   # the sum with the zero products turns -0 into +0
     assert np.array_equal(bits(y.T.contiguous()), bits(torch.from_numpy(want)))
 

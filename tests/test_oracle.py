@@ -254,3 +254,28 @@ def test_dequant64_keeps_bits_fp32_drops():
         assert Fraction(float(w64[l])) == want, l
         lost += Fraction(float(w32[l])) != want
     assert lost > 0   # the fp32 weights are rounded, the fp64 ones are not
+
+
+def _swiglu_pins_hold(fn):
+    """Values the mathematics fixes for silu(g) * u, silu(g) = g / (1 + e^-g)
+    (reflex-llm kernel notes, SwiGLU section):
+      silu(0) = 0; silu(1) = 1 / (1 + e^-1) = 0.7310585786300049;
+      silu(2) = 2 / (1 + e^-2) = 1.7615941559557646;
+      silu(g) - silu(-g) = g for every g (g*s(g) - (-g)*(1 - s(g)), s the logistic);
+      silu(g) -> g as g -> +inf and -> 0 as g -> -inf (40: within 1e-15 relative; -40:
+      below 2e-16 in magnitude);
+      linear in u (u = 0 gives 0, the sign and scale of u carry through)."""
+    g = np.array([0.0, 1.0, 2.0, 40.0, -40.0, 1.0, 1.0, 2.0])
+    u = np.array([3.0, 1.0, 1.0, 1.0, 1.0, 0.0, -2.5, 1.0])
+    out = fn(g, u)
+    ok = (out[0] == 0.0 and abs(out[1] - 0.7310585786300049) <= 1e-15
+          and abs(out[2] - 1.7615941559557646) <= 1e-15
+          and abs(out[3] - 40.0) <= 40.0 * 1e-15 and abs(out[4]) < 2e-16
+          and out[5] == 0.0 and abs(out[6] + 2.5 * 0.7310585786300049) <= 3e-15)
+    gs = synth.rng_for(17).standard_normal(64) * 8.0
+    odd = fn(gs, np.ones_like(gs)) - fn(-gs, np.ones_like(gs))
+    return bool(ok and np.allclose(odd, gs, rtol=1e-13, atol=1e-13))
+
+
+def test_swiglu_pins(orc):
+    assert _swiglu_pins_hold(orc.swiglu)

@@ -49,6 +49,9 @@ MUTANTS = {
     "gemm_unrounded_weights": ("for (int64_t kk = 0; kk < k; kk++) w[kk] = (float)w[kk];", ""),
     "q45_terms_in_fp32": ("w[p] = d * sc * q - dmin * mn;", "w[p] = (float)(d * sc * q) - (float)(dmin * mn);"),
     "gemm_transposed_out": ("y[t * nrows + i] = acc;", "y[i * n + t] = acc;"),
+    "swiglu_exp_sign": ("g[i] / (1.0 + exp(-g[i])) * u[i]", "g[i] / (1.0 + exp(g[i])) * u[i]"),
+    "swiglu_sigmoid_only": ("g[i] / (1.0 + exp(-g[i])) * u[i]", "1.0 / (1.0 + exp(-g[i])) * u[i]"),
+    "swiglu_drops_up": ("g[i] / (1.0 + exp(-g[i])) * u[i]", "g[i] / (1.0 + exp(-g[i]))"),
 }
 
 
@@ -58,7 +61,26 @@ def _load(path):
     L.oracle_dequant.argtypes = [i32, p, p, i64, i64, i64, i64, p]
     L.oracle_gemm.argtypes = [i32, p, p, i64, i64, p, i64, p, i64, p, p, i32]
     L.oracle_dequant64.argtypes = [i32, p, p, i64, i64, i64, i64, p]
+    L.oracle_swiglu.argtypes = [p, p, i64, p]
     return L
+
+
+def _test_oracle_module():
+    spec = importlib.util.spec_from_file_location("t_oracle", os.path.join(ROOT, "tests", "test_oracle.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _swiglu_ok(L):
+    """The SwiGLU pins of test_oracle."""
+    def fn(g, u):
+        g = np.ascontiguousarray(g, np.float64)
+        u = np.ascontiguousarray(u, np.float64)
+        out = np.empty_like(g)
+        L.oracle_swiglu(g.ctypes.data, u.ctypes.data, g.size, out.ctypes.data)
+        return out
+    return _test_oracle_module()._swiglu_pins_hold(fn)
 
 
 def _exact_block_ok(L):
@@ -88,10 +110,7 @@ def _exact_block_ok(L):
 
 def _fp8_grid_ok(L):
     """The hand-written FP8 grid of test_oracle."""
-    spec = importlib.util.spec_from_file_location("t_oracle", os.path.join(ROOT, "tests", "test_oracle.py"))
-    mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
-    codes, scales, want = mod._fp8_grid()
+    codes, scales, want = _test_oracle_module()._fp8_grid()
     out = np.empty((130, 256), np.float32)
     L.oracle_dequant(1002, codes.ctypes.data, scales.ctypes.data, 130, 256, 0, 130, out.ctypes.data)
     return np.array_equal(out, want.astype(np.float32))
@@ -100,7 +119,7 @@ def _fp8_grid_ok(L):
 def _pins_pass(L):
     """True when every golden block, the exact-weight block, the FP8 grid and a
     numpy matmul check agree with library L."""
-    if not _exact_block_ok(L) or not _fp8_grid_ok(L):
+    if not _exact_block_ok(L) or not _fp8_grid_ok(L) or not _swiglu_ok(L):
         return False
     for fx in json.load(open(GOLDEN))["fixtures"]:
         data = np.frombuffer(bytes.fromhex(fx["data"]), np.uint8).copy()
