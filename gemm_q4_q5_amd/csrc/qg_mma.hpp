@@ -261,9 +261,10 @@ __device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
     return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
 }
 
-// Half-group q of staged superblock cb, which is superblock cb0 + cb*stride of x.
-template <int T>
-__device__ __forceinline__ void xhalf_fetch(const MmaArgs &A, int q, int cb0, int stride, XHalf &X) {
+// Half-group q of staged superblock cb, which is superblock cb0 + cb*stride of x
+// (AT: any launch-argument struct with x, n and k).
+template <int T, class AT>
+__device__ __forceinline__ void xhalf_fetch(const AT &A, int q, int cb0, int stride, XHalf &X) {
     const int n = A.n, h = q & 1, r = q >> 1;
     const int t = n == 1 ? 0 : r % n, cg = n == 1 ? r : r / n, g = cg & 3, cb = cg >> 2;
     const _Float16 *p = reinterpret_cast<const _Float16 *>(A.x) + (int64_t)t * A.k + (int64_t)(cb0 + cb * stride) * 256 +
