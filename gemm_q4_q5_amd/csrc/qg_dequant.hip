@@ -15,7 +15,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs A) {
     float *out = A.out + r * (int64_t)A.k + b * 256;
     if (A.type == T_Q4_K || A.type == T_Q5_K) {
         const bool q5 = A.type == T_Q5_K;
-        const RawKq R = load_kq(q5, kq_block(A.data, A.row_bytes, q5 ? 176 : 144, r, (int)b, A.tiled), c);
+        const RawKq R = q5 ? Loader<T_Q5_K>::load(A.data, A.scales, A.row_bytes, r, (int)b, c, A.tiled)
+                           : Loader<T_Q4_K>::load(A.data, A.scales, A.row_bytes, r, (int)b, c, A.tiled);
         const KqCoef cf = kq_coef(R.hdr, kq_lane_consts(c));
         const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
         const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs A) {
             }
         }
     } else if (A.type == T_Q6_K) {
-        const RawQ6 R = load_q6(kq_block(A.data, A.row_bytes, 210, r, (int)b, A.tiled), c);
+        const RawQ6 R = Loader<T_Q6_K>::load(A.data, A.scales, A.row_bytes, r, (int)b, c, A.tiled);
         const int s = c >> 1, h = c & 1;
         const uint32_t sel = R.mis ? kSelMis : kSelAligned;
         const uint32_t av[5] = {R.a.x, R.a.y, R.a.z, R.a.w, R.a4};
@@ -77,18 +78,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs A) {
     }
 }
 
-// Row-major superblocks -> 16-row tiles: thread o writes 16-bit unit o of the tiled
-// copy (every superblock size is even); rows past m in the last tile repeat row m-1.
+// Row-major superblocks -> the 16-row tiled layout (tile_chunk, tile_src): thread o
+// writes 16-bit unit o of the tiled copy (every offset is even); rows past m in the
+// last tile repeat row m-1.
 __global__ __launch_bounds__(256) void pack_tiles_kernel(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
                                                         int64_t m, int64_t row_bytes, int sbytes, int64_t units) {
     const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (o >= units) return;
-    const int64_t half = sbytes / 2, nb = row_bytes / sbytes;
-    const int64_t e = o % half, blk = o / half;   // unit e of tiled superblock blk
-    const int64_t rr = blk & 15, tb = blk >> 4;    // row within the tile, (tile, superblock)
-    const int64_t b = tb % nb, t = tb / nb;
-    const int64_t r = t * 16 + rr < m ? t * 16 + rr : m - 1;
-    dst[o] = src[(r * row_bytes + b * sbytes) / 2 + e];
+    const int64_t half = 8 * (int64_t)sbytes, nb = row_bytes / sbytes;   // 16-bit units per chunk
+    const int e = (int)(o % half) * 2;                                     // byte of the chunk
+    const int64_t ch = o / half;                                           // chunk (tile, superblock)
+    const int64_t b = ch % nb, t = ch / nb;
+    int j = 0;
+    const int off = tile_src(sbytes, e, j);
+    const int64_t r = t * 16 + j < m ? t * 16 + j : m - 1;
+    dst[o] = src[(r * row_bytes + b * sbytes + off) / 2];
 }
 
 hipError_t launch_pack_tiles(const uint8_t *src, uint8_t *dst, int64_t m, int64_t row_bytes, int sbytes,

@@ -113,14 +113,86 @@ __device__ __forceinline__ RawF4 load_f4(const uint8_t *codes, const uint8_t *sc
 }
 
 // ---------------------------------------------------------------------------
-// Superblock b of row r of a K-quant matrix of S-byte superblocks: rows one after
-// another (tiled = 0), or tiles of 16 rows in which superblock b of the tile's 16 rows
-// is stored contiguously (tiled = 1: ((r/16 * nb + b) * 16 + r%16) * S).
-__device__ __forceinline__ const uint8_t *kq_block(const uint8_t *data, int64_t row_bytes, int S, int64_t r, int b,
-                                                   int tiled) {
-    if (!tiled) return data + r * row_bytes + (int64_t)b * S;
-    const int64_t nb = row_bytes / S;
-    return data + (((r >> 4) * nb + b) * 16 + (r & 15)) * (int64_t)S;
+// Superblock b of row r of a K-quant matrix of S-byte superblocks, rows one after
+// another (the layout as stored).
+__device__ __forceinline__ const uint8_t *kq_block(const uint8_t *data, int64_t row_bytes, int S, int64_t r, int b) {
+    return data + r * row_bytes + (int64_t)b * S;
+}
+
+// The 16-row tiled layout (qg_pack_tiles): superblock b of the 16 rows of tile r/16 is
+// one chunk of 16*S bytes at ((r/16 * nb + b) * 16) * S, and inside it every 16-byte
+// piece a lane of the product loads is contiguous with its neighbours' (lane L = 16g +
+// j: row j of the tile, lane group g), so each load instruction of a wave reads one run
+// of bytes:
+//   Q4_K (S = 144): header of row j at 16j; quant bytes 32g..32g+15 of row j at
+//                   256 + 16L, 32g+16..32g+31 at 1280 + 16L.
+//   Q5_K (S = 176): header at 16j; fifth-bit bytes 0..15 at 256 + 16j, 16..31 at
+//                   512 + 16j; quant bytes 32g.. at 768 + 16L, 32g+16.. at 1792 + 16L.
+//   Q6_K (S = 210): g = 2s + h: low-nibble bytes 64s+16h.. at 16L, 64s+32+16h.. at
+//                   1024 + 16L, high-bit bytes 32s+16h.. at 2048 + 16L; the 16 int8
+//                   scales of row j at 3072 + 16j; d at 3328 + 2j.
+// Every byte of the 16 superblocks appears exactly once; rows past m in a last partial
+// tile repeat row m-1.
+__device__ __forceinline__ const uint8_t *tile_chunk(const uint8_t *data, int nb, int S, int64_t r, int b) {
+    return data + (((r >> 4) * nb + b) * 16) * (int64_t)S;
+}
+
+// Byte offset, inside row j's superblock, of byte e (even) of a tiled chunk, and j.
+__device__ __forceinline__ int tile_src(int S, int e, int &j) {
+    if (S == 144) {
+        if (e < 256) { j = e >> 4; return e & 15; }
+        const int hi = e >= 1280, L = ((e - (hi ? 1280 : 256)) >> 4);
+        j = L & 15;
+        return 16 + 32 * (L >> 4) + 16 * hi + (e & 15);
+    }
+    if (S == 176) {
+        if (e < 256) { j = e >> 4; return e & 15; }
+        if (e < 768) { const int hi = e >= 512; j = (e - (hi ? 512 : 256)) >> 4; return 16 + 16 * hi + (e & 15); }
+        const int hi = e >= 1792, L = ((e - (hi ? 1792 : 768)) >> 4);
+        j = L & 15;
+        return 48 + 32 * (L >> 4) + 16 * hi + (e & 15);
+    }
+    // 210
+    if (e < 3072) {
+        const int run = e >> 10, L = (e & 1023) >> 4, g = L >> 4, s = g >> 1, h = g & 1;
+        j = L & 15;
+        return (run == 0 ? 64 * s + 16 * h : (run == 1 ? 64 * s + 32 + 16 * h : 128 + 32 * s + 16 * h)) + (e & 15);
+    }
+    if (e < 3328) { j = (e - 3072) >> 4; return 192 + (e & 15); }
+    j = (e - 3328) >> 1;
+    return 208 + (e & 1);
+}
+
+// Raw loads of chunk c of a tiled superblock (lane group c of row j = r & 15).
+__device__ __forceinline__ RawKq load_kq_tiled(bool q5, const uint8_t *ch, int j, int c) {
+    const int L = 16 * c + j;
+    RawKq r;
+    r.hdr = ld16(ch + 16 * j);
+    if (q5) {
+        r.h0 = ld16(ch + 256 + 16 * j);
+        r.h1 = ld16(ch + 512 + 16 * j);
+        r.q0 = ld16(ch + 768 + 16 * L);
+        r.q1 = ld16(ch + 1792 + 16 * L);
+    } else {
+        r.h0 = r.h1 = make_uint4(0, 0, 0, 0);
+        r.q0 = ld16(ch + 256 + 16 * L);
+        r.q1 = ld16(ch + 1280 + 16 * L);
+    }
+    return r;
+}
+
+__device__ __forceinline__ RawQ6 load_q6_tiled(const uint8_t *ch, int j, int c) {
+    const int L = 16 * c + j, s = c >> 1;
+    RawQ6 r;
+    r.mis = 0;
+    r.a = ld16(ch + 16 * L);
+    r.b = ld16(ch + 1024 + 16 * L);
+    r.h = ld16(ch + 2048 + 16 * L);
+    r.a4 = r.b4 = r.h4 = 0;   // aligned runs: the realigning dword is never used
+    r.s01 = ld8(ch + 3072 + 16 * j + 8 * s);
+    r.s2 = 0;
+    r.d = *reinterpret_cast<const uint16_t *>(ch + 3328 + 2 * j);
+    return r;
 }
 
 // The raw chunk type and loader of a weight type (tiled: K-quants only).
@@ -132,7 +204,8 @@ struct Loader<T_Q4_K> {
     typedef RawKq Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
                                                int b, int c, int tiled) {
-        return load_kq(false, kq_block(data, row_bytes, 144, r, b, tiled), c);
+        if (tiled) return load_kq_tiled(false, tile_chunk(data, (int)(row_bytes / 144), 144, r, b), (int)(r & 15), c);
+        return load_kq(false, kq_block(data, row_bytes, 144, r, b), c);
     }
 };
 
@@ -141,7 +214,8 @@ struct Loader<T_Q5_K> {
     typedef RawKq Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
                                                int b, int c, int tiled) {
-        return load_kq(true, kq_block(data, row_bytes, 176, r, b, tiled), c);
+        if (tiled) return load_kq_tiled(true, tile_chunk(data, (int)(row_bytes / 176), 176, r, b), (int)(r & 15), c);
+        return load_kq(true, kq_block(data, row_bytes, 176, r, b), c);
     }
 };
 
@@ -150,7 +224,8 @@ struct Loader<T_Q6_K> {
     typedef RawQ6 Raw;
     static __device__ __forceinline__ Raw load(const uint8_t *data, const uint8_t *, int64_t row_bytes, int64_t r,
                                                int b, int c, int tiled) {
-        return load_q6(kq_block(data, row_bytes, 210, r, b, tiled), c);
+        if (tiled) return load_q6_tiled(tile_chunk(data, (int)(row_bytes / 210), 210, r, b), (int)(r & 15), c);
+        return load_q6(kq_block(data, row_bytes, 210, r, b), c);
     }
 };
 

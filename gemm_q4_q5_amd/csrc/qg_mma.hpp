@@ -120,42 +120,61 @@ struct MRawOf<T_FP8> {
 // boundary.  Every load is issued from the 4-byte-aligned address below the data;
 // the dword after each run, which the byte-pairing permute needs to realign, is
 // the first dword of another lane's run (q6_extras).
-// row: the row's superblock 0; sbs: bytes from one of the row's superblocks to the
-// next (the superblock size, or 16 times it in the 16-row tiled layout).
+// row: the row's superblock 0 (rows as stored), or the tile's chunk 0 (tiled layout,
+// tile_chunk in qg_loads.hpp: the lane's pieces sit at fixed offsets in the chunk);
+// sbs: bytes from one of the row's superblocks (chunks) to the next.
 template <int T>
 __device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, const uint8_t *srow, int b, int g,
-                                                          int sbs) {
+                                                          int sbs, int tiled) {
     typename MRawOf<T>::type r;
+    const int j = (int)(threadIdx.x & 15), L = 16 * g + j;
     if constexpr (T == T_Q4_K) {
         const uint8_t *blk = row + (int64_t)b * sbs;
-        r.hdr = mld16(blk);
-        r.q0 = mld16(blk + 16 + 32 * g);
-        r.q1 = mld16(blk + 32 + 32 * g);
+        if (tiled) {
+            r.hdr = mld16(blk + 16 * j);
+            r.q0 = mld16(blk + 256 + 16 * L);
+            r.q1 = mld16(blk + 1280 + 16 * L);
+        } else {
+            r.hdr = mld16(blk);
+            r.q0 = mld16(blk + 16 + 32 * g);
+            r.q1 = mld16(blk + 32 + 32 * g);
+        }
     } else if constexpr (T == T_Q5_K) {
         const uint8_t *blk = row + (int64_t)b * sbs;
-        r.hdr = mld16(blk);
-        r.h0 = mld16(blk + 16);
-        r.h1 = mld16(blk + 32);
-        r.q0 = mld16(blk + 48 + 32 * g);
-        r.q1 = mld16(blk + 64 + 32 * g);
+        if (tiled) {
+            r.hdr = mld16(blk + 16 * j);
+            r.h0 = mld16(blk + 256 + 16 * j);
+            r.h1 = mld16(blk + 512 + 16 * j);
+            r.q0 = mld16(blk + 768 + 16 * L);
+            r.q1 = mld16(blk + 1792 + 16 * L);
+        } else {
+            r.hdr = mld16(blk);
+            r.h0 = mld16(blk + 16);
+            r.h1 = mld16(blk + 32);
+            r.q0 = mld16(blk + 48 + 32 * g);
+            r.q1 = mld16(blk + 64 + 32 * g);
+        }
     } else if constexpr (T == T_Q6_K) {
+        // One set of loads at offsets chosen per layout.  Tiled: aligned runs (the
+        // realigning dword is fetched but never used).  Rows: every load issued from the
+        // 4-byte-aligned address below the data.
         const uint8_t *blk = row + (int64_t)b * sbs;
         const int s = g >> 1, h = g & 1;
-        const uint32_t mis = (uint32_t)((uintptr_t)blk & 3u);   // 0 or 2
-        const uint8_t *base = blk - mis;
-        const uint8_t *pa = base + 64 * s + 16 * h;
-        const uint8_t *pb = pa + 32;
-        const uint8_t *ph = base + 128 + 32 * s + 16 * h;
-        r.mis = mis;
-        r.a = mld16(pa);
-        r.b = mld16(pb);
-        r.h = mld16(ph);
-        const uint8_t *ps = base + 192 + 8 * s;
-        const u32x2 s01 = *reinterpret_cast<const u32x2 *>(ps);
+        const int mis = tiled ? 0 : (int)((uintptr_t)blk & 3u);   // 0 or 2
+        const int oa = tiled ? 16 * L : 64 * s + 16 * h - mis;
+        const int ob = tiled ? 1024 + 16 * L : oa + 32;
+        const int oh = tiled ? 2048 + 16 * L : 128 + 32 * s + 16 * h - mis;
+        const int os = tiled ? 3072 + 16 * j + 8 * s : 192 + 8 * s - mis;
+        const int od = tiled ? 3328 + 2 * j : 208;
+        r.mis = (uint32_t)mis;
+        r.a = mld16(blk + oa);
+        r.b = mld16(blk + ob);
+        r.h = mld16(blk + oh);
+        const u32x2 s01 = *reinterpret_cast<const u32x2 *>(blk + os);
         r.s0 = s01.x;
         r.s1 = s01.y;
-        r.s2 = mld4(mis ? ps + 8 : ps + 4);
-        r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+        r.s2 = mld4(blk + os + (mis ? 8 : 4));
+        r.d = *reinterpret_cast<const uint16_t *>(blk + od);
     } else if constexpr (T == T_FP8) {
         const uint8_t *c = row + (int64_t)b * 256 + 32 * g;
         r.a0 = mld16(c);
@@ -169,6 +188,7 @@ __device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, co
         r.q1 = mld16(c + 32 * g + 16);
         r.sc = mld4(srow + (int64_t)b * 16 + 4 * g);
     }
+    (void)L;
     return r;
 }
 
@@ -443,7 +463,7 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             MRawQ6 Ri = R[i];
-            q6_extras(Ri, g);
+            if (__builtin_amdgcn_ballot_w64(Ri.mis != 0)) q6_extras(Ri, g);   // wave-uniform
             const Q6Tile K = q6_tile(Ri, g);
             f4 c1[NG];
 #pragma unroll
@@ -535,7 +555,7 @@ __device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, in
 // turn; every wave steps through every chunk (two barriers per step), whether or
 // not it has superblocks there, so all waves meet the same barriers.
 template <int T, int NT, int NG, int NP, int D>
-__device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int sbs, bool dec, int g, int t,
+__device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int sbs, int tl, bool dec, int g, int t,
                                          const uint8_t *const (&wr)[NT], const uint8_t *const (&sr)[NT], uint4 *lds,
                                          f4 (&acc)[NP][NT][NG]) {
     typedef typename MRawOf<T>::type Raw;
@@ -589,7 +609,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
             const int q = q0 + lane;
             if (cnt > 0) xhalf_fetch<T>(A, q < hq ? q : hq - 1, kw, KW, X);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kw, lastb), g, sbs);
+            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kw, lastb), g, sbs, tl);
             if (cnt > 0) xhalf_commit<T>(q, q < hq, X, xu);   // LDS order within a wave: no barrier
         }
 #pragma unroll
@@ -597,7 +617,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
             if (u + 1 < D) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(sb(u + 1), lastb), g, sbs);
+                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(sb(u + 1), lastb), g, sbs, tl);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (u < cnt) {   // scalar branch
@@ -614,7 +634,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
 #pragma unroll
         for (int u = 0; u < D; ++u)
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(sb(u), lastb), g, sbs);
+            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(sb(u), lastb), g, sbs, tl);
     });
     __syncthreads();
     int chunk = 0;
@@ -636,7 +656,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
             }
             if (it + D < cnt) {   // refill only with a superblock the wave still serves
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], sr[i], min(sb(it + D), lastb), g, sbs);
+                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], sr[i], min(sb(it + D), lastb), g, sbs, tl);
             }
         }
     }
@@ -690,15 +710,15 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 
     const uint8_t *wr[NT];
     const uint8_t *sr[NT];
-    // K-quant superblock bytes; in the 16-row tiled layout a row's superblocks are
-    // 16 of them apart, the row's first at ((r/16) * nb * 16 + r%16) * sbytes.
+    // K-quant superblock bytes; in the 16-row tiled layout a tile's chunks (16
+    // superblocks each) follow one another from (r/16) * nb * 16 * sbytes.
     const int sbytes = S.type == T_Q4_K ? 144 : (S.type == T_Q5_K ? 176 : (S.type == T_Q6_K ? 210 : 0));
     const int sbs = S.tiled ? 16 * sbytes : sbytes;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t r = rows[i] < S.m ? rows[i] : S.m - 1;   // rows past m read row m-1; results dropped
         const bool second = up != 0;
-        const int64_t roff = S.tiled ? ((r >> 4) * A.nb * 16 + (r & 15)) * sbytes : r * S.row_bytes;
+        const int64_t roff = S.tiled ? (r >> 4) * A.nb * 16 * sbytes : r * S.row_bytes;   // tiled: the tile's chunk 0
         wr[i] = (second ? S.data2 : S.data) + roff;
         const uint8_t *sc = second ? S.scales2 : S.scales;
         // NVFP4: one e4m3 scale per 16 weights of the row; FP8: the bf16 scale row
@@ -714,15 +734,15 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 #pragma unroll
             for (int q = 0; q < NG; ++q) ph[a][i][q] = (f4){0.f, 0.f, 0.f, 0.f};
     if ((TS & TS_Q4) && S.type == T_Q4_K)
-        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_Q5) && S.type == T_Q5_K)
-        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_Q6) && S.type == T_Q6_K)
-        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_F4) && S.type == T_NVFP4)
-        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
     else if ((TS & TS_F8) && S.type == T_FP8)
-        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, sbs, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
 
     // The KS phase partials of a row tile, added in phase order:
     //     y = (((p0 + p1) + p2) + ...) + p(KS-1).

@@ -165,9 +165,11 @@ __device__ __forceinline__ int p_row_exp(const PrefillArgs &A, int64_t r) {
         const int S = T == T_Q4_K ? 144 : (T == T_Q5_K ? 176 : 210);
 #pragma unroll 8
         for (int b = 0; b < nb; ++b) {
-            const uint8_t *blk = kq_block(A.data, A.row_bytes, S, r, b, A.tiled);
-            if constexpr (T == T_Q6_K) u = max(u, q6_exp_bound(*reinterpret_cast<const uint16_t *>(blk + 208)));
-            else u = max(u, kq_exp_bound(*reinterpret_cast<const uint32_t *>(blk)));
+            // d (Q6_K) or d | dmin << 16 (Q4_K, Q5_K) of row r's superblock b
+            const uint8_t *f = A.tiled ? tile_chunk(A.data, nb, S, r, b) + (T == T_Q6_K ? 3328 + 2 * (r & 15) : 16 * (r & 15))
+                                       : kq_block(A.data, A.row_bytes, S, r, b) + (T == T_Q6_K ? 208 : 0);
+            if constexpr (T == T_Q6_K) u = max(u, q6_exp_bound(*reinterpret_cast<const uint16_t *>(f)));
+            else u = max(u, kq_exp_bound(*reinterpret_cast<const uint32_t *>(f)));
         }
     } else if constexpr (T == T_FP8) {
         const uint16_t *srow = reinterpret_cast<const uint16_t *>(A.scales + (r >> 7) * (A.row_bytes / 64));

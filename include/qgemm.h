@@ -40,9 +40,11 @@
  *    Row r of a K-quant weight starts at data + r * qg_row_bytes(type, k)
  *    (QG_LAYOUT_ROWS, the layout the superblocks are stored in), or, in the
  *    16-row tiled layout (QG_LAYOUT_TILES, made by qg_pack_tiles), superblock b of
- *    row r sits at data + ((r/16 * (k/256) + b) * 16 + r%16) * S, S the superblock
- *    size: superblock b of 16 consecutive rows is contiguous, so a wave that
- *    streams 16 rows reads one run.  The values are the same; so are the bits of
+ *    the 16 rows of tile r/16 is one chunk of 16*S bytes at data + (r/16 * (k/256)
+ *    + b) * 16 * S, S the superblock size, with the bytes of those 16 superblocks
+ *    arranged so that every 16-byte load of the product kernel reads a run shared
+ *    with its neighbour lanes (the arrangement of each type is documented with
+ *    the loads in qg_loads.hpp).  The values are the same; so are the bits of
  *    every product.
  *  - k must be a multiple of 256 for every type (one superblock; for NVFP4 one
  *    block of 16 scales).  m >= 1.
