@@ -2,9 +2,12 @@
 //
 // Every entry point validates all of its arguments on the host before touching
 // the HIP runtime, so a bad call returns a QG_ERR_* code, launches nothing, and
-// can be exercised without a GPU.  The launch shape of a weight matrix is a pure
-// function of (type, m, k) (TandemLLM Kernels page, "Row invariance": tile tables
-// keyed by the weight's shape, never by the row count).
+// can be exercised without a GPU.  The arithmetic of a weight row -- its K phases
+// and the order their sums are added in -- is a function of (type, m, k) only
+// (TandemLLM Kernels page, "Row invariance": tables keyed by the weight's shape,
+// never by the row count).  How many waves and workgroups carry those phases, and
+// whether x is staged per wave or per workgroup, also follow n: none of it changes
+// a row's instructions or their order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdarg.h>

@@ -56,16 +56,22 @@
  *  - Aliasing: resid may equal y (in-place residual add); any other overlap
  *    between an output and another buffer is undefined.
  *  - Determinism and row invariance ([TK] Row invariance, Verify twins): the
- *    per-row instruction sequence and the reduction order depend only on
- *    (type, m, k), never on n or on the other rows.  For 1 <= n <= 32 the
+ *    arithmetic of a row -- its operands, its K phases and the order their sums
+ *    are added in -- depends only on (type, m, k), never on n or on the other
+ *    rows; the launch shape (waves per workgroup, phases per wave, how x is
+ *    staged) may follow n without touching it.  For 1 <= n <= 32 the
  *    qgemv_* / qgemm_rows / fused calls therefore give bit-identical results
  *    for a given row whether it is called alone (n = 1) or as one of n rows,
  *    each output of a pair/triple equals the corresponding single call bit for
  *    bit, and qgemv_add equals fl32(resid + qgemm_rows(...)).  Repeated calls
  *    return identical bits.  qgemm_prefill is deterministic but carries no such
  *    twin contract ([TK] "Prefill kernels": chunk kernels share work across rows).
- *  - Accuracy: fp32 accumulation; |y - y_exact| stays far inside
- *    2e-3 * sum_k |w||x| for the documented value ranges.
+ *  - Accuracy: each weight enters the product as the exact weight times a power
+ *    of two of its superblock (prefill: of its row), rounded once to fp16
+ *    (relative error <= 2^-11 wherever the scaled weight is an fp16 normal),
+ *    with fp32 accumulation: |y - y_exact| stays within 2e-3 * sum_k |w||x| also
+ *    where the two terms of a Q4_K / Q5_K weight cancel, and an output whose
+ *    weights are all zero is exactly zero (exactly resid for qgemv_add).
  */
 #ifndef QGEMM_H
 #define QGEMM_H
@@ -206,8 +212,10 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
  * prefill GEMM with scales decoded once per (row, sub-block) and one dequantized
  * weight tile shared by all waves of a block): Y[n][m] = X[n][k] W^T for any
  * n >= 1 and every weight type.  Each workgroup dequantizes its weight tile once
- * into fp16 in LDS (the exact weight rounded once, to nearest even; |error| <= 2^-11 |w|)
- * and multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
+ * into fp16 in LDS -- the exact weight times a power of two of its row, rounded
+ * once to nearest even (|error| <= 2^-11 |w| wherever the scaled weight is an fp16
+ * normal); the row's sums are scaled back exactly when stored -- and multiplies
+ * with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
  * y fp32 [n][m].  n up to 2^30; QG_ERR_SHAPE if the call would need more than
  * 2^31 - 1 tiles of Y (64x64 to 128x128 each).  Deterministic; no row-invariance
  * contract ([TK] "Prefill kernels": chunk kernels share work across rows and are

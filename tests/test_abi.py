@@ -99,6 +99,9 @@ def test_gemv_single_validation():
     assert L.qgemv_q5k(FAKE, FAKE, FAKE, 8, 500, None) == -2
     assert L.qgemv_q6k(FAKE, FAKE, FAKE, 0, 512, None) == -2
     assert L.qgemv_nvfp4(FAKE, None, FAKE, FAKE, 8, 512, None) == -1
+    # NVFP4 streams 256 weights per step: k a multiple of 16 but not of 256 is refused
+    assert L.qgemv_nvfp4(FAKE, FAKE, FAKE, FAKE, 8, 272, None) == -2
+    assert L.qgemv_nvfp4(FAKE, FAKE, FAKE, FAKE, 8, 16, None) == -2
     assert L.qgemv_fp8(FAKE, None, FAKE, FAKE, 8, 512, None) == -1
     assert L.qgemv_fp8(FAKE, FAKE, FAKE, FAKE, 8, 640, None) == -2
     assert L.qgemv_q4k(FAKE, FAKE + 8, FAKE, 8, 512, None) == -5
