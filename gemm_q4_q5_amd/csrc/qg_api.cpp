@@ -454,25 +454,11 @@ int qgemm_prefill(const qg_weight *w, const void *x, float *y, int64_t n, void *
     a.k = (int32_t)w->k;
     a.type = w->type;
     a.tiled = w->layout == QG_LAYOUT_TILES;
-    // 128x128 tiles when they give every CU a workgroup (256 CUs); else 128x64 tiles
-    // when they fill 160..256 CUs in one round (their two LDS tile pairs, 96 KB,
-    // leave room for one workgroup per CU); else 64x64 (two per CU).  Measured at
-    // 512 tokens: the 9728-row matrix on 128x128 tiles (304 workgroups) 67 us
-    // against 80 us on 128x64; the 2560 x 9728 matrix on 128x64 (160 workgroups)
-    // 111 us against 119 us on 64x64; at 256 tokens the 4096-row matrix on 64x64
-    // (256 workgroups) beats 128x64 (128).
-    int bm = 64, bn = 64;
-    const int64_t rt128 = (w->m + 127) / 128, rt64 = (w->m + 63) / 64, tt128 = (n + 127) / 128;
-    if (rt128 * tt128 >= 256) {
-        bm = 128;
-        bn = 128;
-    } else if (rt64 * tt128 >= 160 && rt64 * tt128 <= 256) {
-        bm = 128;
-        bn = 64;
-    }
-    if ((w->m + bn - 1) / bn * ((n + bm - 1) / bm) > 0x7fffffff)
-        return fail(QG_ERR_SHAPE, "m = %lld, n = %lld: more than 2^31 - 1 tiles", (long long)w->m, (long long)n);
-    hipError_t e = qg::launch_prefill(a, bm, bn, (hipStream_t)stream);
+    const int64_t blocks = (w->m + qg::kPrefillBlockN - 1) / qg::kPrefillBlockN *
+                           ((n + qg::kPrefillBlockM - 1) / qg::kPrefillBlockM);
+    if (blocks > 0x7fffffff)
+        return fail(QG_ERR_SHAPE, "m = %lld, n = %lld: more than 2^31 - 1 blocks", (long long)w->m, (long long)n);
+    hipError_t e = qg::launch_prefill(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
     g_err.clear();
     return QG_OK;

@@ -18,7 +18,8 @@ struct PrefillArgs {
     int32_t pad;
 };
 
-// bm x bn tile per workgroup: (128, 128), (128, 64) or (64, 64).
-hipError_t launch_prefill(const PrefillArgs &a, int bm, int bn, hipStream_t st);
+// Blocks of 64 tokens x 64 weight rows per workgroup.
+constexpr int kPrefillBlockM = 64, kPrefillBlockN = 64;
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
 
 }  // namespace qg

@@ -217,7 +217,7 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
  * normal); the row's sums are scaled back exactly when stored -- and multiplies
  * with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
  * y fp32 [n][m].  n up to 2^30; QG_ERR_SHAPE if the call would need more than
- * 2^31 - 1 tiles of Y (64x64 to 128x128 each).  Deterministic; no row-invariance
+ * 2^31 - 1 blocks of Y (64 x 64 each).  Deterministic; no row-invariance
  * contract ([TK] "Prefill kernels": chunk kernels share work across rows and are
  * checked by agreement).
  */

@@ -165,7 +165,7 @@ def test_tiles_bytes_and_pack_validation():
 
 
 def test_prefill_shape_limits():
-    """n outside 1..2^30 and calls needing more than 2^31 - 1 tiles of Y are
+    """n outside 1..2^30 and calls needing more than 2^31 - 1 blocks of Y are
     rejected before anything reaches the device."""
     L = qg.lib()
     ref, _k = w(m=8)
@@ -173,4 +173,4 @@ def test_prefill_shape_limits():
     assert L.qgemm_prefill(ref, FAKE, FAKE, (1 << 30) + 1, None) == -2
     big, _b = w(m=1 << 30)
     assert L.qgemm_prefill(big, FAKE, FAKE, 1 << 30, None) == -2
-    assert b"tiles" in L.qg_last_error()
+    assert b"blocks" in L.qg_last_error()

@@ -21,10 +21,8 @@ TYPES = [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4, qg.FP8]
 
 
 @pytest.mark.parametrize("wt", TYPES)
-# (2000, 256, 2050) takes the 128x128 tile (single-buffered loop), (1000, 512, 2000)
-# the 128x64 tile (pipelined loop), (1000, 256, 2100) the 64x64 tile in a grid of
-# more than 512 workgroups (single-buffered loop), all ragged in both dimensions;
-# the others take the 64x64 tile (pipelined loop).
+# 64-token x 64-row blocks: one superblock (k = 256) up to 4 (k = 1024); ragged in
+# tokens and rows (a last block with 1..63 of each); one block, and grids of thousands.
 @pytest.mark.parametrize("m,k,n", [(300, 1024, 130), (64, 256, 1), (130, 768, 17), (1000, 512, 256),
                                    (2000, 256, 2050), (1000, 512, 2000), (1000, 256, 2100)])
 def test_prefill_vs_oracle(wt, m, k, n):
@@ -54,8 +52,8 @@ def test_prefill_deterministic():
     assert np.array_equal(a, b)
 
 
-# (m, k) with k tokens of an identity input: the 64x64 tile pipelined and (1500 x
-# 2048, 768 workgroups) single-buffered, 128x64 and 128x128.
+# (m, k) with k tokens of an identity input: square and ragged blocks, up to 8
+# superblocks per row.
 @pytest.mark.parametrize("wt", TYPES)
 @pytest.mark.parametrize("m,k", [(300, 512), (1500, 2048), (1250, 1280), (2048, 2048)])
 def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
@@ -75,9 +73,9 @@ def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
 
 
 def test_prefill_more_token_tiles_than_a_grid_dimension():
-    """8.4 M tokens in 128x128 tiles: 65,537 token tiles, more than a second grid
+    """8.4 M tokens in 64-token blocks: 131,074 token blocks, more than a second grid
     dimension holds; the grid is one-dimensional.  x is generated on the GPU and
-    sampled tokens (first, last, both sides of the 65,535-tile mark) are checked
+    sampled tokens (first, last, both sides of the 65,535 x 128 mark) are checked
     against the oracle."""
     import torch
     m, k = 100, 256
