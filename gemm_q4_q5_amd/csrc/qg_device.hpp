@@ -156,6 +156,70 @@ __device__ __forceinline__ KqScaled kq_scaled(uint4 hdr, const KqLane &L, int u)
     return k;
 }
 
+// Exact split of the lane's two sub-blocks of a Q4_K / Q5_K superblock for the matrix
+// cores.  With A = d*sc and B = dmin*m (both exact in fp32) and an integer c in
+// [0, qmax] (the nearest to B/A, 0 when A = 0), every weight of the sub-block is
+//     w = d*sc*q - dmin*m = A*(q - c) + r,    r = A*c - B,
+// where A*(q - c) = d * 2^14 * o with o = (q - c)*sc*2^-14 an fp16 value computed
+// exactly (|q - c|*sc <= 31*63 < 2^11) by one packed fp16 fma from the quant's
+// fp16-subnormal bits: o = v*S + C with v = q*2^-24 (low sub-block) or q*2^-20 (high),
+// S = sc*2^10 or sc*2^6, C = -c*sc*2^-14.  As c is the nearest integer to B/A, |r| <=
+// |A|/2 and every term is bounded by the weight it belongs to: |r| <= |w| and
+// |A*(q - c)| <= 2|w| for q != c (clamping c to [0, qmax] only happens where the two
+// terms share a sign), so sums over o*x and r*sum(x) carry rounding errors that
+// scale with sum|w||x| whatever cancels inside a weight, and a sub-block of zero
+// weights gives o = 0 and r = 0 exactly.
+struct KqSplit {
+    uint32_t s0, c0, s1, c1;   // packed fp16 S and C of sub-blocks 2c (low nibbles) and 2c+1
+    float r0, r1;              // their remainders r
+    float dd;                  // d * 2^14
+};
+
+__device__ __forceinline__ void kq_split_one(float d, float dmin, uint32_t sc, uint32_t m, float sscale, float qmax,
+                                             uint32_t &S, uint32_t &C, float &r) {
+    const float a = d * (float)sc, b = dmin * (float)m;   // exact
+    float c = __builtin_rintf(b * __builtin_amdgcn_rcpf(a));
+    c = __builtin_fminf(__builtin_fmaxf(c, 0.0f), qmax);
+    c = a != 0.0f ? c : 0.0f;
+    r = __builtin_fmaf(a, c, -b);
+    const _Float16 sh = (_Float16)((float)sc * sscale);                        // exact: <= 64512
+    const _Float16 ch = (_Float16)(-c * (float)sc * (1.0f / 16384.0f));       // exact: c*sc <= 1953
+    S = as_u32((h2){sh, sh});
+    C = as_u32((h2){ch, ch});
+}
+
+__device__ __forceinline__ KqSplit kq_split(uint4 hdr, const KqLane &L, float qmax) {
+    uint32_t sc, mn;
+    kq_scale_min(hdr, L, sc, mn);
+    const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
+    KqSplit k;
+    k.dd = d * 16384.0f;
+    kq_split_one(d, dmin, sc & 0xFFu, mn & 0xFFu, 1024.0f, qmax, k.s0, k.c0, k.r0);
+    kq_split_one(d, dmin, (sc >> 8) & 0xFFu, (mn >> 8) & 0xFFu, 64.0f, qmax, k.s1, k.c1, k.r1);
+    return k;
+}
+
+// v*S + C on both fp16 halves, one rounding each (v_pk_fma_f16).
+__device__ __forceinline__ uint32_t pkfma(uint32_t v, uint32_t S, uint32_t C) {
+    return as_u32(__builtin_elementwise_fma(as_h2(v), as_h2(S), as_h2(C)));
+}
+
+// Sum of the sixteen fp16 values in two 16-byte units, in a fixed order (two per
+// v_dot2_f32_f16 against ones), in fp32.
+__device__ __forceinline__ float hsum16(uint4 a, uint4 b) {
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float s = 0.0f;
+    s = __builtin_amdgcn_fdot2(as_h2(a.x), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(a.y), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(a.z), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(a.w), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(b.x), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(b.y), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(b.z), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(b.w), one, s, false);
+    return s;
+}
+
 // fp16(a*v + b) for the two fp16 halves of v, one rounding each
 // (v_fma_mixlo_f16 / v_fma_mixhi_f16).
 __device__ __forceinline__ uint32_t mix2(uint32_t v, float a, float b) {

@@ -223,6 +223,10 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_m
 //              inside one 128-wide scale block)
 constexpr int kUnitsPerTok = 9;
 constexpr int kZeroUnits = 9;
+// Q4_K / Q5_K: the ninth unit of (cb, g, t) holds the fp32 sums of x over the lane
+// group's two sub-blocks, half by half: {sum over positions 0..15 of sub-block 2g,
+// of 2g+1, over positions 16..31 of 2g, of 2g+1} (see xhalf_commit).
+constexpr int kXSumUnit = 8;
 
 template <int T>
 __device__ __forceinline__ void slot_pieces(int g, int s, int &o0, int &o1) {
@@ -315,6 +319,11 @@ __device__ __forceinline__ void xhalf_commit(int q, bool st, const XHalf &X, uin
         }
         if (st) u[i] = v;
     }
+    if constexpr (T == T_Q4_K || T == T_Q5_K) {
+        // loads 0, 1: positions 16h..16h+15 of sub-block 2g; loads 2, 3: of 2g+1
+        const float p0 = hsum16(X.v[0], X.v[1]), p1 = hsum16(X.v[2], X.v[3]);
+        if (st) reinterpret_cast<float2 *>(xs + (q >> 1) * kUnitsPerTok + kXSumUnit)[q & 1] = make_float2(p0, p1);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -322,14 +331,16 @@ __device__ __forceinline__ void xhalf_commit(int q, bool st, const XHalf &X, uin
 // positions 4s..4s+3 of sub-block 2g (low nibbles) and of sub-block 2g+1 (high
 // nibbles).  Masked in place, each 16-bit half is an fp16 subnormal carrying the
 // quant in its mantissa: q * 2^-24 (low nibble, bits 0..3, Q5_K's fifth bit at 4) or
-// q * 2^-20 (high nibble, bits 4..7, fifth bit at 8); the sub-block's coefficients
-// absorb the 2^24 / 2^20, so one mixed-precision fma per weight gives
-//     w' = fp16(a*q + b),   a = d*sc*2^(15-U),  b = -dmin*m*2^(15-U)
-// with a*q + b exact in fp32 before its one rounding.  Slot order of the step:
+// q * 2^-20 (high nibble, bits 4..7, fifth bit at 8); one packed fp16 fma per two
+// weights gives the exact operands o = (q - c)*sc*2^-14 of the split w = d*2^14*o +
+// r (kq_split).  Slot order of the step:
 //     (4s, 4s+2), (4s+1, 4s+3) of sub-block 2g, then the same of 2g+1.
-typedef KqScaled KqTile;   // a0 carries 2^24, a1 2^20 (the quants' subnormal scales)
+typedef KqSplit KqTile;
 
-__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, int g) { return kq_scaled(R.hdr, kq_lane_consts(g), kq_exp_bound(R.hdr.x)); }
+template <bool Q5>
+__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, int g) {
+    return kq_split(R.hdr, kq_lane_consts(g), Q5 ? 31.0f : 15.0f);
+}
 
 template <bool Q5>
 __device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, int s) {
@@ -342,7 +353,7 @@ __device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, i
         const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
         q5_fifth(hw[s] >> (2 * g), lo02, lo13, hi02, hi13);
     }
-    return mk_h8(mix2(lo02, K.a0, K.b0), mix2(lo13, K.a0, K.b0), mix2(hi02, K.a1, K.b1), mix2(hi13, K.a1, K.b1));
+    return mk_h8(pkfma(lo02, K.s0, K.c0), pkfma(lo13, K.s0, K.c0), pkfma(hi02, K.s1, K.c1), pkfma(hi13, K.s1, K.c1));
 }
 
 // Q6_K.  Lane chunk g = half h6 = g >> 1, quarter q6 = g & 1 (positions 16*q6 ..
@@ -441,10 +452,13 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
                                     f4 (&acc)[NT][NG]) {
     const uint4 *const(&xv)[NG] = xa;   // LDS reads at their use; other waves hide the latency
     if constexpr (T == T_Q4_K || T == T_Q5_K) {
-        // c = sum_k w'*x over the superblock (one MFMA chain); y += 2^(U-15) * c.
+        // c = sum_k o*x over the superblock (one MFMA chain); y += d*2^14 * c, then
+        // y += sum_j r_j * X_j over the eight sub-blocks j (X_j = sum of x over
+        // sub-block j, staged beside x) with two fp32 MFMAs: lane group g holds the
+        // r and X of sub-blocks 2g (first) and 2g+1 (second).
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            const KqTile K = kq_tile(R[i], g);
+            const KqTile K = kq_tile<T == T_Q5_K>(R[i], g);
             f4 c1[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -455,9 +469,15 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
                 for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
             }
 #pragma unroll
-            for (int q = 0; q < NG; ++q)
+            for (int q = 0; q < NG; ++q) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(pow2f(K.u - 15), c1[q][e], acc[i][q][e]);
+                for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(K.dd, c1[q][e], acc[i][q][e]);
+                const uint4 xp = xv[q][kXSumUnit];
+                const float x0 = __builtin_bit_cast(float, xp.x) + __builtin_bit_cast(float, xp.z);
+                const float x1 = __builtin_bit_cast(float, xp.y) + __builtin_bit_cast(float, xp.w);
+                acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(x0, K.r0, acc[i][q], 0, 0, 0);
+                acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, K.r1, acc[i][q], 0, 0, 0);
+            }
         }
     } else if constexpr (T == T_Q6_K) {
 #pragma unroll
@@ -698,7 +718,10 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     // Ring depth: three superblocks with one phase per wave; with several, four (two
     // in 16-wave workgroups, which have 128 registers, and one there with four phases
     // of two token groups, whose accumulators alone take 32 of them).
-    constexpr int D = NP == 1 ? kDepth : (WV <= 8 ? 4 : (NP == 4 && NG == 2 ? 1 : 2));
+    // The all-types 16-wave instance for two token groups keeps two (its decode path
+    // never has more than one superblock per wave: 8 * n * count <= 256 with n > 16).
+    constexpr int D = NP == 1 ? ((TS == TS_ALL && NG == 2 && WV == 16) ? 2 : kDepth)
+                              : (WV <= 8 ? 4 : (NP == 4 && NG == 2 ? 1 : 2));
     const int j = lane & 15, g = lane >> 4;
     const int up = SW ? (rt & 1) : 0;   // SwiGLU: 0 for a gate tile group, 1 for an up one
     const int64_t unit = SW ? (int64_t)(bid - S.wg_begin) * (tpw >> 1) + (rt >> 1)

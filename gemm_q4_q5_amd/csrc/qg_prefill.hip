@@ -12,10 +12,13 @@
 // superblock, in the operand's k-slot order, and every wave reads them from there.
 // Per superblock and step a wave reads NG x fragments and issues NT*NG MFMAs.
 //
-// Weight operands are fp16: each weight scaled by a power of two 2^(15-U) of its
-// row, then rounded once to nearest even.  U bounds the magnitudes of the row's
-// weights (|w| < 2^U; the largest of its superblocks' bounds, read from their d /
-// dmin, or from FP8's block scales, before the K loop), so the scaled weight never
+// Q4_K / Q5_K weights enter through the exact split of the 1..32-token product
+// (kq_split: an exact fp16 operand per weight, one MFMA chain per superblock scaled
+// by d, and the sub-blocks' remainders times their x sums through fp32 MFMAs), so no
+// weight is rounded.  Q6_K and FP8 operands are fp16: each weight scaled by a power of
+// two 2^(15-U) of its row, then rounded once to nearest even.  U bounds the magnitudes
+// of the row's weights (|w| < 2^U; the largest of its superblocks' bounds, read from
+// their d, or from FP8's block scales, before the K loop), so the scaled weight never
 // overflows fp16, and a weight no smaller than 2^(U-29) is an fp16 normal (|error| <=
 // 2^-11 |w|); an exactly zero weight stays zero.  The row's sums are scaled back
 // (exactly) when stored.  NVFP4 weights are exact in fp16 and need no scale.
@@ -35,8 +38,8 @@
 
 namespace qg {
 
-// U of weight row r: |w| < 2^U for every weight of the row.  K-quants: the largest
-// superblock bound (kq_exp_bound, q6_exp_bound); FP8: |code| <= 448 < 2^9 and a bf16
+// U of weight row r: |w| < 2^U for every weight of the row.  Q6_K: the largest
+// superblock bound (q6_exp_bound); FP8: |code| <= 448 < 2^9 and a bf16
 // scale with exponent field Es is below 2^(Es-126), so |w| < 2^(Es-117), clamped at
 // -110 (the tiniest scales) so that 2^(15-U) stays an fp32 normal.  Reads only the
 // d / dmin / scale fields, which the K loop reads again from cache.
@@ -44,15 +47,14 @@ template <int T>
 __device__ __forceinline__ int p_row_exp(const PrefillArgs &A, int64_t r) {
     int u = -1000;
     const int nb = A.k / 256;
-    if constexpr (T == T_Q4_K || T == T_Q5_K || T == T_Q6_K) {
-        const int S = T == T_Q4_K ? 144 : (T == T_Q5_K ? 176 : 210);
+    if constexpr (T == T_Q6_K) {
+        const int S = 210;
 #pragma unroll 8
         for (int b = 0; b < nb; ++b) {
-            // d (Q6_K) or d | dmin << 16 (Q4_K, Q5_K) of row r's superblock b
-            const uint8_t *f = A.tiled ? tile_chunk(A.data, nb, S, r, b) + (T == T_Q6_K ? 3328 + 2 * (r & 15) : 16 * (r & 15))
-                                       : kq_block(A.data, A.row_bytes, S, r, b) + (T == T_Q6_K ? 208 : 0);
-            if constexpr (T == T_Q6_K) u = max(u, q6_exp_bound(*reinterpret_cast<const uint16_t *>(f)));
-            else u = max(u, kq_exp_bound(*reinterpret_cast<const uint32_t *>(f)));
+            // d of row r's superblock b
+            const uint8_t *f = A.tiled ? tile_chunk(A.data, nb, S, r, b) + 3328 + 2 * (r & 15)
+                                       : kq_block(A.data, A.row_bytes, S, r, b) + 208;
+            u = max(u, q6_exp_bound(*reinterpret_cast<const uint16_t *>(f)));
         }
     } else if constexpr (T == T_FP8) {
         const uint16_t *srow = reinterpret_cast<const uint16_t *>(A.scales + (r >> 7) * (A.row_bytes / 64));
@@ -64,13 +66,14 @@ __device__ __forceinline__ int p_row_exp(const PrefillArgs &A, int64_t r) {
     return u;
 }
 
-// Whether the weights are scaled (every type but NVFP4).
+// Whether the weights are scaled by a power of two of their row (Q6_K, FP8; Q4_K and
+// Q5_K use the exact split, NVFP4 is exact in fp16).
 template <int T>
-constexpr bool p_scaled() { return T != T_NVFP4; }
+constexpr bool p_scaled() { return T == T_Q6_K || T == T_FP8; }
 
 // Per-tile coefficients of one superblock for the lane's row (u = the row's U).
 struct PCoefKq {
-    KqScaled k;
+    KqSplit k;
 };
 struct PCoefQ6 {
     float a[4], b[4];   // group g weight = fp16(a[g] * v + b[g]), v the magic value (q6_oct)
@@ -100,7 +103,8 @@ __device__ __forceinline__ typename PCoefOf<T>::type p_coef(const typename MRawO
                                                             int g, int u) {
     typename PCoefOf<T>::type c;
     if constexpr (T == T_Q4_K || T == T_Q5_K) {
-        c.k = kq_scaled(R.hdr, L, u);
+        c.k = kq_split(R.hdr, L, T == T_Q5_K ? 31.0f : 15.0f);
+        (void)u;
     } else if constexpr (T == T_Q6_K) {
         // a_g = d * sc_g (* 1/4 for groups 2, 3) * 2^(15-u): at most 18 significant bits,
         // and so are a_g * 1056 and a_g * 384 (two set bits each): a_g * v + b_g is
@@ -133,11 +137,12 @@ __device__ __forceinline__ void q6p_steps(const MRawQ6 &R, const PCoefQ6 &C, h8 
                mix2(o.v[3][1], C.a[3], C.b[3]));
 }
 
-// Q4_K / Q5_K operand of step s with the quant dword byte-paired first ([b0 b2 b1
-// b3]), so that its slots hold positions 4s..4s+3 of sub-block 2g and then 4s..4s+3
-// of 2g+1 in order: the x of a step is two runs of four, staged without permutes.
+// Q4_K / Q5_K operand of step s (the exact split's o, kq_split) with the quant dword
+// byte-paired first ([b0 b2 b1 b3]), so that its slots hold positions 4s..4s+3 of
+// sub-block 2g and then 4s..4s+3 of 2g+1 in order: the x of a step is two runs of
+// four, staged without permutes.
 template <bool Q5>
-__device__ __forceinline__ h8 pkq_step(const MRawKq &R, const KqScaled &K, int g, int s) {
+__device__ __forceinline__ h8 pkq_step(const MRawKq &R, const KqSplit &K, int g, int s) {
     const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
     const uint32_t w = pair_bytes(qw[s], qw[s], kSelAligned), w8 = w >> 8;
     uint32_t lo01 = w & 0x000F000Fu, lo23 = w8 & 0x000F000Fu;
@@ -146,7 +151,7 @@ __device__ __forceinline__ h8 pkq_step(const MRawKq &R, const KqScaled &K, int g
         const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
         q5_fifth(pair_bytes(hw[s], hw[s], kSelAligned) >> (2 * g), lo01, lo23, hi01, hi23);
     }
-    return mk_h8(mix2(lo01, K.a0, K.b0), mix2(lo23, K.a0, K.b0), mix2(hi01, K.a1, K.b1), mix2(hi23, K.a1, K.b1));
+    return mk_h8(pkfma(lo01, K.s0, K.c0), pkfma(lo23, K.s0, K.c0), pkfma(hi01, K.s1, K.c1), pkfma(hi23, K.s1, K.c1));
 }
 
 // The weight operand of step s (0..7) for the types with one step per operand.
@@ -186,6 +191,10 @@ __device__ __forceinline__ void p_xcommit(int q, const XHalf &X, uint4 *xs) {
     for (int i = 0; i < 4; ++i) {
         const uint2 p0 = xhalf_piece<T>(X, i, 0), p1 = xhalf_piece<T>(X, i, 1);
         u[i] = make_uint4(p0.x, p0.y, p1.x, p1.y);
+    }
+    if constexpr (T == T_Q4_K || T == T_Q5_K) {   // the sub-block sums, as in xhalf_commit
+        const float s0 = hsum16(X.v[0], X.v[1]), s1 = hsum16(X.v[2], X.v[3]);
+        reinterpret_cast<float2 *>(xs + (q >> 1) * kUnitsPerTok + kXSumUnit)[q & 1] = make_float2(s0, s1);
     }
 }
 
@@ -266,6 +275,38 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
             dword(std::integral_constant<int, 1>{});
             dword(std::integral_constant<int, 2>{});
             dword(std::integral_constant<int, 3>{});
+        } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
+            // One chain per superblock: y += d*2^14 * sum(o*x) + sum_j r_j * X_j.
+            f4 c1[NT][NG];
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) c1[i][q] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                h8 xa[NG];
+#pragma unroll
+                for (int q = 0; q < NG; ++q) xa[q] = u4h8(xl[16 * q * kUnitsPerTok + s]);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    const h8 b = p_step<T>(R[i], C[i], g, s);
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) c1[i][q] = mfma(xa[q], b, c1[i][q]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                const uint4 xp = xl[16 * q * kUnitsPerTok + kXSumUnit];
+                const float x0 = __builtin_bit_cast(float, xp.x) + __builtin_bit_cast(float, xp.z);
+                const float x1 = __builtin_bit_cast(float, xp.y) + __builtin_bit_cast(float, xp.w);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(C[i].k.dd, c1[i][q][e], acc[i][q][e]);
+                    acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(x0, C[i].k.r0, acc[i][q], 0, 0, 0);
+                    acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, C[i].k.r1, acc[i][q], 0, 0, 0);
+                }
+            }
         } else {
 #pragma unroll
             for (int s = 0; s < 8; ++s) {

@@ -66,10 +66,13 @@
  *    bit, and qgemv_add equals fl32(resid + qgemm_rows(...)).  Repeated calls
  *    return identical bits.  qgemm_prefill is deterministic but carries no such
  *    twin contract ([TK] "Prefill kernels": chunk kernels share work across rows).
- *  - Accuracy: each weight enters the product as the exact weight times a power
- *    of two of its superblock (prefill: of its row), rounded once to fp16
- *    (relative error <= 2^-11 wherever the scaled weight is an fp16 normal),
- *    with fp32 accumulation: |y - y_exact| stays within 2e-3 * sum_k |w||x| also
+ *  - Accuracy: a Q4_K / Q5_K weight enters the product exactly, split as
+ *    d*sc*(q - c) + r with c the integer nearest to dmin*m/(d*sc) (an exact fp16
+ *    operand times d, and a per-sub-block fp32 remainder r times the sub-block's
+ *    sum of x), both parts bounded by the weight; Q6_K, FP8 and NVFP4 weights
+ *    enter as the exact weight times a power of two, rounded once to fp16
+ *    (relative error <= 2^-11 wherever the scaled weight is an fp16 normal).
+ *    With fp32 accumulation |y - y_exact| stays within 2e-3 * sum_k |w||x| also
  *    where the two terms of a Q4_K / Q5_K weight cancel, and an output whose
  *    weights are all zero is exactly zero (exactly resid for qgemv_add).
  */
@@ -211,11 +214,11 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
  * Prefill-chunk GEMM on the matrix cores ([PF] Path E / E5: tensor-core K-quant
  * prefill GEMM with scales decoded once per (row, sub-block) and one dequantized
  * weight tile shared by all waves of a block): Y[n][m] = X[n][k] W^T for any
- * n >= 1 and every weight type.  Each workgroup dequantizes its weight tile once
- * into fp16 in LDS -- the exact weight times a power of two of its row, rounded
- * once to nearest even (|error| <= 2^-11 |w| wherever the scaled weight is an fp16
- * normal); the row's sums are scaled back exactly when stored -- and multiplies
- * with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
+ * n >= 1 and every weight type.  Each wave decodes the weights of its 16 rows
+ * once per 64 tokens into MFMA operands in registers (Q4_K / Q5_K: the exact split
+ * described under Accuracy; the others: the exact weight times a power of two of
+ * its row, rounded once to fp16, the row's sums scaled back exactly when stored)
+ * and multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
  * y fp32 [n][m].  n up to 2^30; QG_ERR_SHAPE if the call would need more than
  * 2^31 - 1 blocks of Y (64 x 64 each).  Deterministic; no row-invariance
  * contract ([TK] "Prefill kernels": chunk kernels share work across rows and are

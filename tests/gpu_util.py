@@ -63,9 +63,12 @@ def prefill_row_exp(wtype, data, scales, m, k):
 
 
 def prefill_operand(wtype, data, scales, m, k):
-    """What the prefill's fp16 weight operand stands for, in weight units (fp64): the
-    oracle's exact weight times 2^(15-U) of its row, rounded once to fp16, times
+    """What the prefill's weight operands stand for, in weight units (fp64).  Q4_K /
+    Q5_K: the oracle's exact weight (the exact split rounds no weight).  Q6_K, FP8,
+    NVFP4: the exact weight times 2^(15-U) of its row, rounded once to fp16, times
     2^(U-15)."""
-    u = prefill_row_exp(wtype, data, scales, m, k)[:, None].astype(np.float64)
     w = oracle.dequant64(wtype, data, scales, m, k)
+    if wtype in (synth.Q4_K, synth.Q5_K):
+        return w
+    u = prefill_row_exp(wtype, data, scales, m, k)[:, None].astype(np.float64)
     return (w * 2.0 ** (15 - u)).astype(np.float16).astype(np.float64) * 2.0 ** (u - 15)

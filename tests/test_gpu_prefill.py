@@ -1,11 +1,12 @@
 """GPU parity of the MFMA prefill GEMM against the CPU oracle.
 
-The weight operand is the exact weight times a power of two of its row, rounded
-once to fp16 (round to nearest even), so the output is held to |y - y_ref| <=
-2e-3 * sum|w||x| against the oracle's fp64 product, and -- much tighter -- to
-fp32-accumulation error against the fp64 product of the oracle's exact weights
-rounded that way (which pins the MFMA operand layout).  An identity input returns
-the operand itself, compared bit for bit.
+Q6_K / FP8 / NVFP4 weight operands are the exact weight times a power of two of its
+row, rounded once to fp16 (round to nearest even); Q4_K / Q5_K weights enter through
+an exact split (no rounding).  The output is held to |y - y_ref| <= 2e-3 * sum|w||x|
+against the oracle's fp64 product, and -- much tighter -- to fp32-accumulation error
+against the fp64 product of what the operands stand for (which pins the MFMA operand
+layout).  An identity input returns the operand itself (Q6_K / FP8 / NVFP4: bit for
+bit; Q4_K / Q5_K: the exact weight to within two fp32 roundings).
 """
 import numpy as np
 import pytest
@@ -57,16 +58,24 @@ def test_prefill_deterministic():
 @pytest.mark.parametrize("wt", TYPES)
 @pytest.mark.parametrize("m,k", [(300, 512), (1500, 2048), (1250, 1280), (2048, 2048)])
 def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
-    """x = I (k tokens): y[t][r] is the kernel's fp16 operand for w[r][t] (one
-    nonzero product, exact in fp32) scaled back by its row's power of two, which must
-    equal the oracle's exact weight scaled by it and rounded once to fp16 -- not the
-    fp32 weight rounded again, which differs where the fp32 value lands on an fp16
-    tie."""
+    """x = I (k tokens): y[t][r] is what the kernel makes of w[r][t].  Q6_K, FP8,
+    NVFP4: its fp16 operand (one nonzero product, exact in fp32) scaled back by its
+    row's power of two, which must equal the oracle's exact weight scaled by it and
+    rounded once to fp16 -- not the fp32 weight rounded again, which differs where
+    the fp32 value lands on an fp16 tie.  Q4_K / Q5_K (exact split): d*sc*(q - c)
+    exact in fp32 plus the fp32 remainder r = d*sc*c - dmin*m, two roundings of
+    quantities no larger than the weight, so |y - w| <= 2^-22 |w| and zero weights
+    give exactly zero."""
     import torch
     print(f"prefill operand type={wt} m={m} k={k}", flush=True)
     w, data, scales = weight(wt, m, k, 231)
     y = qg.qgemm_prefill(w, x_dev(np.eye(k, dtype=np.float16)))
     torch.cuda.synchronize()
+    if wt in (qg.Q4_K, qg.Q5_K):
+        exact = oracle.dequant64(wt, data, scales, m, k)
+        got = y.T.contiguous().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - exact) <= 2.0 ** -22 * np.abs(exact))
+        return
     want = prefill_operand(wt, data, scales, m, k).astype(np.float32)
     want = want + np.float32(0.0)   # the sum with the zero products turns -0 into +0
     assert np.array_equal(bits(y.T.contiguous()), bits(torch.from_numpy(want)))
