@@ -298,6 +298,33 @@ __device__ __forceinline__ Q6Oct q6_oct(uint32_t a, uint32_t b, uint32_t hq) {
     return o;
 }
 
+// The same eight pairs without the magic exponent: groups 0, 1 hold q in bits 0..5
+// of each 16-bit half (the fp16 subnormal q * 2^-24), groups 2, 3 hold it in bits
+// 4..9 (q * 2^-20).
+__device__ __forceinline__ Q6Oct q6_sub_oct(uint32_t a, uint32_t b, uint32_t hq) {
+    const uint32_t a8 = a >> 8, b8 = b >> 8, h8 = hq >> 8;
+    const uint32_t h4 = hq << 4, h2 = hq << 2, h84 = h8 << 4, h82 = h8 << 2;
+    Q6Oct o;
+    o.v[0][0] = and_or(h4, 0x00300030u, a & 0x000F000Fu);
+    o.v[0][1] = and_or(h84, 0x00300030u, a8 & 0x000F000Fu);
+    o.v[1][0] = and_or(h2, 0x00300030u, b & 0x000F000Fu);
+    o.v[1][1] = and_or(h82, 0x00300030u, b8 & 0x000F000Fu);
+    o.v[2][0] = and_or(h4, 0x03000300u, a & 0x00F000F0u);
+    o.v[2][1] = and_or(h84, 0x03000300u, a8 & 0x00F000F0u);
+    o.v[3][0] = and_or(h2, 0x03000300u, b & 0x00F000F0u);
+    o.v[3][1] = and_or(h82, 0x03000300u, b8 & 0x00F000F0u);
+    return o;
+}
+
+// Packed S, C of a Q6_K group with int8 scale sc for q6_sub_oct values: v*S + C =
+// (q - 32)*sc*2^-16 (S = sc*2^8 for groups 0, 1, sc*2^4 for 2, 3; C = -sc*2^-11, exact),
+// exact in fp16 while |(q - 32)*sc| <= 2^11 (|sc| <= 64), else rounded once.
+__device__ __forceinline__ void q6_sc(float sc, bool hi, uint32_t &S, uint32_t &C) {
+    const _Float16 s = (_Float16)(sc * (hi ? 16.0f : 256.0f)), c = (_Float16)(sc * (-1.0f / 2048.0f));
+    S = as_u32((h2){s, s});
+    C = as_u32((h2){c, c});
+}
+
 // Signed 8-bit field at bit `off` of w (an int8 Q6_K scale), as fp32.
 __device__ __forceinline__ float i8_at(uint32_t w, int off) {
     return (float)(int32_t)__builtin_amdgcn_sbfe(w, off, 8);

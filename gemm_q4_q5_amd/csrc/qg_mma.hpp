@@ -359,12 +359,13 @@ __device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, i
 // Q6_K.  Lane chunk g = half h6 = g >> 1, quarter q6 = g & 1 (positions 16*q6 ..
 // 16*q6+15 of each of the four 32-weight groups of the half).  Dword i of the
 // runs A (groups 0, 2), B (groups 1, 3) and H (high bits) covers positions 4i..4i+3;
-// q6_oct gives 1024 + q for groups 0, 1 and 256 + 4q for groups 2, 3 (byte-paired,
-// positions in natural order).  Step s = 2i + e takes groups 2e (pairs 0, 1) and
-// then 2e + 1, positions 4i .. 4i+3 of each.  The weight operand is
-//   (v - 1056) * sc   (groups 0, 1)      (v - 384) * (sc/4)   (groups 2, 3).
+// q6_sub_oct gives the quant as an fp16 subnormal, q * 2^-24 for groups 0, 1 and
+// q * 2^-20 for groups 2, 3 (byte-paired, positions in natural order).  Step s = 2i + e
+// takes groups 2e (pairs 0, 1) and then 2e + 1, positions 4i .. 4i+3 of each.  The
+// weight operand is (q - 32)*sc*2^-16 (q6_sc: one packed fma per two weights); the
+// superblock's chain is scaled by d*2^16.
 struct Q6Tile {
-    h2 S[4];
+    uint32_t S[4], C[4];
     float d;
 };
 
@@ -388,11 +389,11 @@ __device__ __forceinline__ Q6Tile q6_tile(const MRawQ6 &R, int g) {
     const int sh = 8 * (g & 1);
     // scale of group grp: sub-block 8*h6 + 2*grp + q6 (grp 0, 1 in l0; 2, 3 in l1)
     Q6Tile k;
-    k.S[0] = h2c(i8_at(l0, sh));
-    k.S[1] = h2c(i8_at(l0, sh + 16));
-    k.S[2] = h2c(0.25f * i8_at(l1, sh));
-    k.S[3] = h2c(0.25f * i8_at(l1, sh + 16));
-    k.d = f16lo(R.d);
+    q6_sc(i8_at(l0, sh), false, k.S[0], k.C[0]);
+    q6_sc(i8_at(l0, sh + 16), false, k.S[1], k.C[1]);
+    q6_sc(i8_at(l1, sh), true, k.S[2], k.C[2]);
+    q6_sc(i8_at(l1, sh + 16), true, k.S[3], k.C[3]);
+    k.d = f16lo(R.d) * 65536.0f;
     return k;
 }
 
@@ -409,12 +410,11 @@ __device__ __forceinline__ uint32_t run_pair(uint4 v, uint32_t extra, uint32_t s
 template <int I>
 __device__ __forceinline__ void q6_steps(const MRawQ6 &R, const Q6Tile &K, h8 &b0, h8 &b1) {
     const uint32_t sel = R.mis ? kSelMis : kSelAligned;
-    const Q6Oct o = q6_oct(run_pair<I>(R.a, R.a4, sel), run_pair<I>(R.b, R.b4, sel), run_pair<I>(R.h, R.h4, sel));
-    const h2 B01 = h2c(-1056.0f), B23 = h2c(-384.0f);
-    b0 = mk_h8(as_u32((as_h2(o.v[0][0]) + B01) * K.S[0]), as_u32((as_h2(o.v[0][1]) + B01) * K.S[0]),
-               as_u32((as_h2(o.v[1][0]) + B01) * K.S[1]), as_u32((as_h2(o.v[1][1]) + B01) * K.S[1]));
-    b1 = mk_h8(as_u32((as_h2(o.v[2][0]) + B23) * K.S[2]), as_u32((as_h2(o.v[2][1]) + B23) * K.S[2]),
-               as_u32((as_h2(o.v[3][0]) + B23) * K.S[3]), as_u32((as_h2(o.v[3][1]) + B23) * K.S[3]));
+    const Q6Oct o = q6_sub_oct(run_pair<I>(R.a, R.a4, sel), run_pair<I>(R.b, R.b4, sel), run_pair<I>(R.h, R.h4, sel));
+    b0 = mk_h8(pkfma(o.v[0][0], K.S[0], K.C[0]), pkfma(o.v[0][1], K.S[0], K.C[0]), pkfma(o.v[1][0], K.S[1], K.C[1]),
+               pkfma(o.v[1][1], K.S[1], K.C[1]));
+    b1 = mk_h8(pkfma(o.v[2][0], K.S[2], K.C[2]), pkfma(o.v[2][1], K.S[2], K.C[2]), pkfma(o.v[3][0], K.S[3], K.C[3]),
+               pkfma(o.v[3][1], K.S[3], K.C[3]));
 }
 
 // NVFP4 step s: codes 8s .. 8s+7 of the lane's 64 (low nibble first), scale s >> 1.
@@ -718,9 +718,10 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     // Ring depth: three superblocks with one phase per wave; with several, four (two
     // in 16-wave workgroups, which have 128 registers, and one there with four phases
     // of two token groups, whose accumulators alone take 32 of them).
-    // The all-types 16-wave instance for two token groups keeps two (its decode path
-    // never has more than one superblock per wave: 8 * n * count <= 256 with n > 16).
-    constexpr int D = NP == 1 ? ((TS == TS_ALL && NG == 2 && WV == 16) ? 2 : kDepth)
+    // 16-wave instances for two token groups that can hold Q6_K keep two (their
+    // decode path never has more than one superblock per wave: 8 * n * count <= 256
+    // with n > 16).
+    constexpr int D = NP == 1 ? (((TS & TS_Q6) && NG == 2 && WV == 16) ? 2 : kDepth)
                               : (WV <= 8 ? 4 : (NP == 4 && NG == 2 ? 1 : 2));
     const int j = lane & 15, g = lane >> 4;
     const int up = SW ? (rt & 1) : 0;   // SwiGLU: 0 for a gate tile group, 1 for an up one

@@ -12,16 +12,15 @@
 // superblock, in the operand's k-slot order, and every wave reads them from there.
 // Per superblock and step a wave reads NG x fragments and issues NT*NG MFMAs.
 //
-// Q4_K / Q5_K weights enter through the exact split of the 1..32-token product
-// (kq_split: an exact fp16 operand per weight, one MFMA chain per superblock scaled
-// by d, and the sub-blocks' remainders times their x sums through fp32 MFMAs), so no
-// weight is rounded.  Q6_K and FP8 operands are fp16: each weight scaled by a power of
-// two 2^(15-U) of its row, then rounded once to nearest even.  U bounds the magnitudes
-// of the row's weights (|w| < 2^U; the largest of its superblocks' bounds, read from
-// their d, or from FP8's block scales, before the K loop), so the scaled weight never
-// overflows fp16, and a weight no smaller than 2^(U-29) is an fp16 normal (|error| <=
-// 2^-11 |w|); an exactly zero weight stays zero.  The row's sums are scaled back
-// (exactly) when stored.  NVFP4 weights are exact in fp16 and need no scale.
+// Weight operands are those of the 1..32-token product: Q4_K / Q5_K through the exact
+// split (kq_split: an exact fp16 operand per weight, one MFMA chain per superblock
+// scaled by d, the sub-blocks' remainders times their x sums through fp32 MFMAs), so
+// no weight is rounded; Q6_K as (q - 32)*sc*2^-16 in fp16 (exact for |sc| <= 64, else
+// rounded once), one chain per superblock scaled by d*2^16; NVFP4 exact.  FP8 operands
+// are the weight times a power of two 2^(15-U) of its row, rounded once to fp16: U
+// bounds the row's weights (read from its block scales before the K loop), so the
+// scaled weight never overflows fp16 and a weight no smaller than 2^(U-29) is an fp16
+// normal (|error| <= 2^-11 |w|); the row's sums are scaled back exactly when stored.
 //
 // Per superblock b: b+1's weights and x are loaded into registers while b is
 // computed; a barrier; b+1's x is written to the (single) LDS buffer; a barrier.
@@ -38,45 +37,34 @@
 
 namespace qg {
 
-// U of weight row r: |w| < 2^U for every weight of the row.  Q6_K: the largest
-// superblock bound (q6_exp_bound); FP8: |code| <= 448 < 2^9 and a bf16
+// U of weight row r (FP8; 15 for the others): |w| < 2^U for every weight of the row.  FP8: |code| <= 448 < 2^9 and a bf16
 // scale with exponent field Es is below 2^(Es-126), so |w| < 2^(Es-117), clamped at
 // -110 (the tiniest scales) so that 2^(15-U) stays an fp32 normal.  Reads only the
 // d / dmin / scale fields, which the K loop reads again from cache.
 template <int T>
 __device__ __forceinline__ int p_row_exp(const PrefillArgs &A, int64_t r) {
-    int u = -1000;
-    const int nb = A.k / 256;
-    if constexpr (T == T_Q6_K) {
-        const int S = 210;
-#pragma unroll 8
-        for (int b = 0; b < nb; ++b) {
-            // d of row r's superblock b
-            const uint8_t *f = A.tiled ? tile_chunk(A.data, nb, S, r, b) + 3328 + 2 * (r & 15)
-                                       : kq_block(A.data, A.row_bytes, S, r, b) + 208;
-            u = max(u, q6_exp_bound(*reinterpret_cast<const uint16_t *>(f)));
-        }
-    } else if constexpr (T == T_FP8) {
+    int u = 15;
+    if constexpr (T == T_FP8) {
+        const int nb = A.k / 256;
         const uint16_t *srow = reinterpret_cast<const uint16_t *>(A.scales + (r >> 7) * (A.row_bytes / 64));
+        u = -1000;
 #pragma unroll 8
         for (int b = 0; b < 2 * nb; ++b) u = max(u, max((int)((srow[b] >> 7) & 0xFFu) - 117, -110));
-    } else {
-        u = 15;
     }
     return u;
 }
 
-// Whether the weights are scaled by a power of two of their row (Q6_K, FP8; Q4_K and
-// Q5_K use the exact split, NVFP4 is exact in fp16).
+// Whether the weights are scaled by a power of two of their row (FP8; Q4_K and Q5_K
+// use the exact split, Q6_K a per-superblock chain scaled by d, NVFP4 is exact in fp16).
 template <int T>
-constexpr bool p_scaled() { return T == T_Q6_K || T == T_FP8; }
+constexpr bool p_scaled() { return T == T_FP8; }
 
 // Per-tile coefficients of one superblock for the lane's row (u = the row's U).
 struct PCoefKq {
     KqSplit k;
 };
 struct PCoefQ6 {
-    float a[4], b[4];   // group g weight = fp16(a[g] * v + b[g]), v the magic value (q6_oct)
+    Q6Tile k;
 };
 struct PCoefF8 {
     float a[2];         // block h weight = fp16(a[h] * code)
@@ -106,14 +94,8 @@ __device__ __forceinline__ typename PCoefOf<T>::type p_coef(const typename MRawO
         c.k = kq_split(R.hdr, L, T == T_Q5_K ? 31.0f : 15.0f);
         (void)u;
     } else if constexpr (T == T_Q6_K) {
-        // a_g = d * sc_g (* 1/4 for groups 2, 3) * 2^(15-u): at most 18 significant bits,
-        // and so are a_g * 1056 and a_g * 384 (two set bits each): a_g * v + b_g is
-        // d * sc_g * (q - 32) * 2^(15-u) before the fma's one rounding.
-        const uint32_t l0 = __builtin_amdgcn_alignbyte(R.s1, R.s0, R.mis);
-        const uint32_t l1 = __builtin_amdgcn_alignbyte(R.s2, R.s1, R.mis);
-        q6_coefs(l0, l1, f16lo(R.d) * pow2f(15 - u), g & 1, c.a);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c.b[q] = (q < 2 ? -1056.0f : -384.0f) * c.a[q];
+        c.k = q6_tile(R, g);
+        (void)u;
     } else if constexpr (T == T_FP8) {
         // code * s * 2^(15-u): at most 4 + 8 significant bits, rounded once
         c.a[0] = bf16_lo(R.sc) * pow2f(15 - u);
@@ -124,17 +106,6 @@ __device__ __forceinline__ typename PCoefOf<T>::type p_coef(const typename MRawO
     (void)L;
     (void)g;
     return c;
-}
-
-// Q6_K steps 2I and 2I+1 with the row's scale folded in (one mixed fma per weight).
-template <int I>
-__device__ __forceinline__ void q6p_steps(const MRawQ6 &R, const PCoefQ6 &C, h8 &b0, h8 &b1) {
-    const uint32_t sel = R.mis ? kSelMis : kSelAligned;
-    const Q6Oct o = q6_oct(run_pair<I>(R.a, R.a4, sel), run_pair<I>(R.b, R.b4, sel), run_pair<I>(R.h, R.h4, sel));
-    b0 = mk_h8(mix2(o.v[0][0], C.a[0], C.b[0]), mix2(o.v[0][1], C.a[0], C.b[0]), mix2(o.v[1][0], C.a[1], C.b[1]),
-               mix2(o.v[1][1], C.a[1], C.b[1]));
-    b1 = mk_h8(mix2(o.v[2][0], C.a[2], C.b[2]), mix2(o.v[2][1], C.a[2], C.b[2]), mix2(o.v[3][0], C.a[3], C.b[3]),
-               mix2(o.v[3][1], C.a[3], C.b[3]));
 }
 
 // Q4_K / Q5_K operand of step s (the exact split's o, kq_split) with the quant dword
@@ -252,6 +223,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
             C[i] = p_coef<T>(R[i], L, g, u[i]);
         }
         if constexpr (T == T_Q6_K) {
+            // One chain per superblock: y += d*2^16 * sum(o*x) (q6_tile, q6_steps).
+            f4 c1[NT][NG];
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) c1[i][q] = (f4){0.f, 0.f, 0.f, 0.f};
             auto dword = [&](auto I) __attribute__((always_inline)) {
                 constexpr int II = decltype(I)::value;
                 h8 xa0[NG], xa1[NG];
@@ -263,11 +240,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
                     h8 b0, b1;
-                    q6p_steps<II>(R[i], C[i], b0, b1);
+                    q6_steps<II>(R[i], C[i].k, b0, b1);
 #pragma unroll
                     for (int q = 0; q < NG; ++q) {
-                        acc[i][q] = mfma(xa0[q], b0, acc[i][q]);
-                        acc[i][q] = mfma(xa1[q], b1, acc[i][q]);
+                        c1[i][q] = mfma(xa0[q], b0, c1[i][q]);
+                        c1[i][q] = mfma(xa1[q], b1, c1[i][q]);
                     }
                 }
             };
@@ -275,6 +252,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
             dword(std::integral_constant<int, 1>{});
             dword(std::integral_constant<int, 2>{});
             dword(std::integral_constant<int, 3>{});
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int q = 0; q < NG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][q][e] = __builtin_fmaf(C[i].k.d, c1[i][q][e], acc[i][q][e]);
         } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
             // One chain per superblock: y += d*2^14 * sum(o*x) + sum_j r_j * X_j.
             f4 c1[NT][NG];

@@ -64,11 +64,18 @@ def prefill_row_exp(wtype, data, scales, m, k):
 
 def prefill_operand(wtype, data, scales, m, k):
     """What the prefill's weight operands stand for, in weight units (fp64).  Q4_K /
-    Q5_K: the oracle's exact weight (the exact split rounds no weight).  Q6_K, FP8,
-    NVFP4: the exact weight times 2^(15-U) of its row, rounded once to fp16, times
-    2^(U-15)."""
+    Q5_K: the oracle's exact weight (the exact split rounds no weight).  Q6_K: d times
+    the fp16 rounding of sc*(q - 32)*2^-16, times 2^16 (the integer sc*(q - 32) is the
+    exact weight over its superblock's d).  FP8, NVFP4: the exact weight times 2^(15-U)
+    of its row, rounded once to fp16, times 2^(U-15)."""
     w = oracle.dequant64(wtype, data, scales, m, k)
     if wtype in (synth.Q4_K, synth.Q5_K):
         return w
+    if wtype == synth.Q6_K:
+        blk = np.ascontiguousarray(data).reshape(m, k // 256, 210)
+        d = blk[..., 208:210].copy().view(np.float16)[..., 0].astype(np.float64)   # [m, nb]
+        d = np.repeat(d, 256, axis=1)
+        ki = np.divide(w, d, out=np.zeros_like(w), where=d != 0)
+        return d * (ki * 2.0 ** -16).astype(np.float16).astype(np.float64) * 2.0 ** 16
     u = prefill_row_exp(wtype, data, scales, m, k)[:, None].astype(np.float64)
     return (w * 2.0 ** (15 - u)).astype(np.float16).astype(np.float64) * 2.0 ** (u - 15)

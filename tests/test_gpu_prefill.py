@@ -1,8 +1,9 @@
 """GPU parity of the MFMA prefill GEMM against the CPU oracle.
 
-Q6_K / FP8 / NVFP4 weight operands are the exact weight times a power of two of its
-row, rounded once to fp16 (round to nearest even); Q4_K / Q5_K weights enter through
-an exact split (no rounding).  The output is held to |y - y_ref| <= 2e-3 * sum|w||x|
+FP8 / NVFP4 weight operands are the exact weight times a power of two of its row,
+rounded once to fp16 (round to nearest even); Q6_K operands are (q - 32)*sc*2^-16 in
+fp16 with d applied per superblock; Q4_K / Q5_K weights enter through an exact split
+(no rounding).  The output is held to |y - y_ref| <= 2e-3 * sum|w||x|
 against the oracle's fp64 product, and -- much tighter -- to fp32-accumulation error
 against the fp64 product of what the operands stand for (which pins the MFMA operand
 layout).  An identity input returns the operand itself (Q6_K / FP8 / NVFP4: bit for
@@ -58,11 +59,12 @@ def test_prefill_deterministic():
 @pytest.mark.parametrize("wt", TYPES)
 @pytest.mark.parametrize("m,k", [(300, 512), (1500, 2048), (1250, 1280), (2048, 2048)])
 def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
-    """x = I (k tokens): y[t][r] is what the kernel makes of w[r][t].  Q6_K, FP8,
-    NVFP4: its fp16 operand (one nonzero product, exact in fp32) scaled back by its
-    row's power of two, which must equal the oracle's exact weight scaled by it and
-    rounded once to fp16 -- not the fp32 weight rounded again, which differs where
-    the fp32 value lands on an fp16 tie.  Q4_K / Q5_K (exact split): d*sc*(q - c)
+    """x = I (k tokens): y[t][r] is what the kernel makes of w[r][t].  FP8, NVFP4:
+    its fp16 operand (one nonzero product, exact in fp32) scaled back by its row's
+    power of two, which must equal the oracle's exact weight scaled by it and rounded
+    once to fp16 -- not the fp32 weight rounded again, which differs where the fp32
+    value lands on an fp16 tie.  Q6_K: d times the fp16 operand (q - 32)*sc*2^-16
+    times 2^16, exact in fp32.  Q4_K / Q5_K (exact split): d*sc*(q - c)
     exact in fp32 plus the fp32 remainder r = d*sc*c - dmin*m, two roundings of
     quantities no larger than the weight, so |y - w| <= 2^-22 |w| and zero weights
     give exactly zero."""
