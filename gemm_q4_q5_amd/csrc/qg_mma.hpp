@@ -356,6 +356,23 @@ __device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, i
     return mk_h8(pkfma(lo02, K.s0, K.c0), pkfma(lo13, K.s0, K.c0), pkfma(hi02, K.s1, K.c1), pkfma(hi13, K.s1, K.c1));
 }
 
+// The same operands with the quant dword byte-paired first ([b0 b2 b1 b3]), so that
+// the slots of step s hold positions 4s..4s+3 of sub-block 2g and then 4s..4s+3 of
+// 2g+1 in order: the x of a step is two runs of four, which a stager can write
+// without permutes (the prefill's staging, p_xcommit).
+template <bool Q5>
+__device__ __forceinline__ h8 pkq_step(const MRawKq &R, const KqTile &K, int g, int s) {
+    const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+    const uint32_t w = pair_bytes(qw[s], qw[s], kSelAligned), w8 = w >> 8;
+    uint32_t lo01 = w & 0x000F000Fu, lo23 = w8 & 0x000F000Fu;
+    uint32_t hi01 = w & 0x00F000F0u, hi23 = w8 & 0x00F000F0u;
+    if (Q5) {
+        const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
+        q5_fifth(pair_bytes(hw[s], hw[s], kSelAligned) >> (2 * g), lo01, lo23, hi01, hi23);
+    }
+    return mk_h8(pkfma(lo01, K.s0, K.c0), pkfma(lo23, K.s0, K.c0), pkfma(hi01, K.s1, K.c1), pkfma(hi23, K.s1, K.c1));
+}
+
 // Q6_K.  Lane chunk g = half h6 = g >> 1, quarter q6 = g & 1 (positions 16*q6 ..
 // 16*q6+15 of each of the four 32-weight groups of the half).  Dword i of the
 // runs A (groups 0, 2), B (groups 1, 3) and H (high bits) covers positions 4i..4i+3;
@@ -447,7 +464,7 @@ __device__ __forceinline__ void q6_dword(const MRawQ6 &R, const Q6Tile &K, const
 // ---------------------------------------------------------------------------
 // One superblock of NT weight tiles for NG token groups.  xa[q] = the lane's nine
 // units of the superblock for token group q (or the zeros), read up front.
-template <int T, int NT, int NG>
+template <int T, int NT, int NG, bool PAIRED = false>
 __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int g, const uint4 *const (&xa)[NG],
                                     f4 (&acc)[NT][NG]) {
     const uint4 *const(&xv)[NG] = xa;   // LDS reads at their use; other waves hide the latency
@@ -464,7 +481,7 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
             for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const h8 b = kq_step<T == T_Q5_K>(R[i], K, g, s);
+                const h8 b = PAIRED ? pkq_step<T == T_Q5_K>(R[i], K, g, s) : kq_step<T == T_Q5_K>(R[i], K, g, s);
 #pragma unroll
                 for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
             }

@@ -41,41 +41,16 @@ def bits(t):
     return t.detach().contiguous().view(torch.int32).cpu().numpy()
 
 
-def prefill_row_exp(wtype, data, scales, m, k):
-    """The prefill's per-row scale exponent U (|w| < 2^U for every weight of the row),
-    restated from the fields: Q4_K / Q5_K max over superblocks of max(Ed - 3, Em - 8),
-    Q6_K max of Ed - 2 (Ed, Em the fp16 exponent fields of d, dmin), FP8 max over the
-    row's block scales of max(Es - 117, -110) (Es the bf16 exponent field), NVFP4 15."""
-    if wtype == synth.NVFP4:
-        return np.full(m, 15, np.int64)
-    if wtype == synth.FP8:
-        s = np.ascontiguousarray(scales).view(np.uint16).astype(np.int64)   # [ceil(m/128), k/128]
-        u = np.maximum(((s >> 7) & 0xFF) - 117, -110).max(axis=1)
-        return u[np.arange(m) // 128]
-    S = synth.BLOCK_BYTES[wtype]
-    blk = np.ascontiguousarray(data).reshape(m, k // 256, S).astype(np.int64)
-    if wtype == synth.Q6_K:
-        ed = (blk[..., 209] >> 2) & 31
-        return (ed - 2).max(axis=1)
-    ed = (blk[..., 1] >> 2) & 31
-    em = (blk[..., 3] >> 2) & 31
-    return np.maximum(ed - 3, em - 8).max(axis=1)
-
-
 def prefill_operand(wtype, data, scales, m, k):
-    """What the prefill's weight operands stand for, in weight units (fp64).  Q4_K /
-    Q5_K: the oracle's exact weight (the exact split rounds no weight).  Q6_K: d times
-    the fp16 rounding of sc*(q - 32)*2^-16, times 2^16 (the integer sc*(q - 32) is the
-    exact weight over its superblock's d).  FP8, NVFP4: the exact weight times 2^(15-U)
-    of its row, rounded once to fp16, times 2^(U-15)."""
+    """What the prefill's weight operands stand for, in weight units (fp64): the
+    oracle's exact weight, except Q6_K, whose operand is the fp16 rounding of
+    sc*(q - 32)*2^-16 (exact for |sc| <= 64) scaled by d*2^16 (the integer sc*(q - 32)
+    is the exact weight over its superblock's d)."""
     w = oracle.dequant64(wtype, data, scales, m, k)
-    if wtype in (synth.Q4_K, synth.Q5_K):
+    if wtype != synth.Q6_K:
         return w
-    if wtype == synth.Q6_K:
-        blk = np.ascontiguousarray(data).reshape(m, k // 256, 210)
-        d = blk[..., 208:210].copy().view(np.float16)[..., 0].astype(np.float64)   # [m, nb]
-        d = np.repeat(d, 256, axis=1)
-        ki = np.divide(w, d, out=np.zeros_like(w), where=d != 0)
-        return d * (ki * 2.0 ** -16).astype(np.float16).astype(np.float64) * 2.0 ** 16
-    u = prefill_row_exp(wtype, data, scales, m, k)[:, None].astype(np.float64)
-    return (w * 2.0 ** (15 - u)).astype(np.float16).astype(np.float64) * 2.0 ** (u - 15)
+    blk = np.ascontiguousarray(data).reshape(m, k // 256, 210)
+    d = blk[..., 208:210].copy().view(np.float16)[..., 0].astype(np.float64)   # [m, nb]
+    d = np.repeat(d, 256, axis=1)
+    ki = np.divide(w, d, out=np.zeros_like(w), where=d != 0)
+    return d * (ki * 2.0 ** -16).astype(np.float16).astype(np.float64) * 2.0 ** 16

@@ -1,13 +1,13 @@
 """GPU parity of the MFMA prefill GEMM against the CPU oracle.
 
-FP8 / NVFP4 weight operands are the exact weight times a power of two of its row,
-rounded once to fp16 (round to nearest even); Q6_K operands are (q - 32)*sc*2^-16 in
-fp16 with d applied per superblock; Q4_K / Q5_K weights enter through an exact split
-(no rounding).  The output is held to |y - y_ref| <= 2e-3 * sum|w||x|
+The prefill's operands are the 1..32-token product's: NVFP4 and FP8 codes exact in
+fp16 with their scales applied per block, Q6_K (q - 32)*sc*2^-16 in fp16 (exact for
+|sc| <= 64) with d applied per superblock, Q4_K / Q5_K through the exact split (no
+rounding).  The output is held to |y - y_ref| <= 2e-3 * sum|w||x|
 against the oracle's fp64 product, and -- much tighter -- to fp32-accumulation error
 against the fp64 product of what the operands stand for (which pins the MFMA operand
-layout).  An identity input returns the operand itself (Q6_K / FP8 / NVFP4: bit for
-bit; Q4_K / Q5_K: the exact weight to within two fp32 roundings).
+layout).  An identity input returns what each weight becomes (Q6_K / FP8 / NVFP4: bit
+for bit; Q4_K / Q5_K: the exact weight to within two fp32 roundings).
 """
 import numpy as np
 import pytest
@@ -59,27 +59,24 @@ def test_prefill_deterministic():
 @pytest.mark.parametrize("wt", TYPES)
 @pytest.mark.parametrize("m,k", [(300, 512), (1500, 2048), (1250, 1280), (2048, 2048)])
 def test_prefill_weight_operand_is_exact_weight_rounded_once(wt, m, k):
-    """x = I (k tokens): y[t][r] is what the kernel makes of w[r][t].  FP8, NVFP4:
-    its fp16 operand (one nonzero product, exact in fp32) scaled back by its row's
-    power of two, which must equal the oracle's exact weight scaled by it and rounded
-    once to fp16 -- not the fp32 weight rounded again, which differs where the fp32
-    value lands on an fp16 tie.  Q6_K: d times the fp16 operand (q - 32)*sc*2^-16
-    times 2^16, exact in fp32.  Q4_K / Q5_K (exact split): d*sc*(q - c)
-    exact in fp32 plus the fp32 remainder r = d*sc*c - dmin*m, two roundings of
-    quantities no larger than the weight, so |y - w| <= 2^-22 |w| and zero weights
-    give exactly zero."""
+    """x = I (k tokens): y[t][r] is what the kernel makes of w[r][t] alone.  NVFP4,
+    FP8, Q6_K: one nonzero product of exact fp16 values scaled by an exact factor, so y
+    equals prefill_operand bit for bit (the exact weight; for Q6_K with |sc| > 64 its
+    fp16-rounded operand times d).  Q4_K / Q5_K (exact split): d*sc*(q - c) exact in
+    fp32 plus the fp32 remainder r = d*sc*c - dmin*m, two roundings of quantities no
+    larger than the weight, so |y - w| <= 2^-22 |w| and zero weights give exactly
+    zero."""
     import torch
     print(f"prefill operand type={wt} m={m} k={k}", flush=True)
     w, data, scales = weight(wt, m, k, 231)
     y = qg.qgemm_prefill(w, x_dev(np.eye(k, dtype=np.float16)))
     torch.cuda.synchronize()
+    want = prefill_operand(wt, data, scales, m, k)
     if wt in (qg.Q4_K, qg.Q5_K):
-        exact = oracle.dequant64(wt, data, scales, m, k)
         got = y.T.contiguous().cpu().numpy().astype(np.float64)
-        assert np.all(np.abs(got - exact) <= 2.0 ** -22 * np.abs(exact))
+        assert np.all(np.abs(got - want) <= 2.0 ** -22 * np.abs(want))
         return
-    want = prefill_operand(wt, data, scales, m, k).astype(np.float32)
-    want = want + np.float32(0.0)   # the sum with the zero products turns -0 into +0
+    want = want.astype(np.float32) + np.float32(0.0)   # the sum with the zero products turns -0 into +0
     assert np.array_equal(bits(y.T.contiguous()), bits(torch.from_numpy(want)))
 
 
