@@ -125,6 +125,7 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     // gate group handing its sums to the up group, which stores silu(g) * u.
     const int pair = sw ? 2 : 1;   // tile groups per block of 16 output rows
     a.x = x;
+    a.nmagic = n >= 2 ? (uint32_t)((1ull << 32) / (uint64_t)n + 1) : 0u;
     a.nseg = sw ? 1 : nseg;
     a.k = (int32_t)k;
     a.nb = (int32_t)(k / 256);

@@ -120,52 +120,44 @@ struct MRawOf<T_FP8> {
 // boundary.  Every load is issued from the 4-byte-aligned address below the data;
 // the dword after each run, which the byte-pairing permute needs to realign, is
 // the first dword of another lane's run (q6_extras).
-// row: the row's superblock 0 (rows as stored), or the tile's chunk 0 (tiled layout,
-// tile_chunk in qg_loads.hpp: the lane's pieces sit at fixed offsets in the chunk);
-// sbs: bytes from one of the row's superblocks (chunks) to the next.
+// base: the wave's tile, uniform across the wave (rows as stored: its first row's
+// superblock 0; tiled layout, tile_chunk in qg_loads.hpp: its chunk 0), off: the
+// lane's byte offset from it (rows: (row - first row) * row bytes; tiled: 0), so
+// that every load is a uniform base plus a 32-bit lane offset; sbs: bytes from one
+// superblock (chunk) to the next.  srow: the lane's scale row (NVFP4, FP8).
 template <int T>
-__device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, const uint8_t *srow, int b, int g,
-                                                          int sbs, int tiled) {
+__device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *base, uint32_t off, const uint8_t *srow,
+                                                          int b, int g, int sbs, int tiled) {
     typename MRawOf<T>::type r;
-    const int j = (int)(threadIdx.x & 15), L = 16 * g + j;
+    const uint32_t j = threadIdx.x & 15, L = 16 * (uint32_t)g + j;
     if constexpr (T == T_Q4_K) {
-        const uint8_t *blk = row + (int64_t)b * sbs;
-        if (tiled) {
-            r.hdr = mld16(blk + 16 * j);
-            r.q0 = mld16(blk + 256 + 16 * L);
-            r.q1 = mld16(blk + 1280 + 16 * L);
-        } else {
-            r.hdr = mld16(blk);
-            r.q0 = mld16(blk + 16 + 32 * g);
-            r.q1 = mld16(blk + 32 + 32 * g);
-        }
+        const uint8_t *blk = base + (int64_t)b * sbs;
+        const uint32_t oh = tiled ? 16 * j : off, oq = tiled ? 256 + 16 * L : off + 16 + 32 * (uint32_t)g;
+        r.hdr = mld16(blk + oh);
+        r.q0 = mld16(blk + oq);
+        r.q1 = mld16(blk + oq + (tiled ? 1024 : 16));
     } else if constexpr (T == T_Q5_K) {
-        const uint8_t *blk = row + (int64_t)b * sbs;
-        if (tiled) {
-            r.hdr = mld16(blk + 16 * j);
-            r.h0 = mld16(blk + 256 + 16 * j);
-            r.h1 = mld16(blk + 512 + 16 * j);
-            r.q0 = mld16(blk + 768 + 16 * L);
-            r.q1 = mld16(blk + 1792 + 16 * L);
-        } else {
-            r.hdr = mld16(blk);
-            r.h0 = mld16(blk + 16);
-            r.h1 = mld16(blk + 32);
-            r.q0 = mld16(blk + 48 + 32 * g);
-            r.q1 = mld16(blk + 64 + 32 * g);
-        }
+        const uint8_t *blk = base + (int64_t)b * sbs;
+        const uint32_t oh = tiled ? 16 * j : off, o5 = tiled ? 256 + 16 * j : off + 16;
+        const uint32_t oq = tiled ? 768 + 16 * L : off + 48 + 32 * (uint32_t)g;
+        r.hdr = mld16(blk + oh);
+        r.h0 = mld16(blk + o5);
+        r.h1 = mld16(blk + o5 + (tiled ? 256 : 16));
+        r.q0 = mld16(blk + oq);
+        r.q1 = mld16(blk + oq + (tiled ? 1024 : 16));
     } else if constexpr (T == T_Q6_K) {
         // One set of loads at offsets chosen per layout.  Tiled: aligned runs (the
         // realigning dword is fetched but never used).  Rows: every load issued from the
-        // 4-byte-aligned address below the data.
-        const uint8_t *blk = row + (int64_t)b * sbs;
+        // 4-byte-aligned address below the data.  (A per-lane pointer here: the
+        // uniform-base form measured slower for this type.)
+        const uint8_t *blk = base + off + (int64_t)b * sbs;
         const int s = g >> 1, h = g & 1;
         const int mis = tiled ? 0 : (int)((uintptr_t)blk & 3u);   // 0 or 2
-        const int oa = tiled ? 16 * L : 64 * s + 16 * h - mis;
-        const int ob = tiled ? 1024 + 16 * L : oa + 32;
-        const int oh = tiled ? 2048 + 16 * L : 128 + 32 * s + 16 * h - mis;
-        const int os = tiled ? 3072 + 16 * j + 8 * s : 192 + 8 * s - mis;
-        const int od = tiled ? 3328 + 2 * j : 208;
+        const int oa = tiled ? 16 * (int)L : 64 * s + 16 * h - mis;
+        const int ob = tiled ? 1024 + 16 * (int)L : oa + 32;
+        const int oh = tiled ? 2048 + 16 * (int)L : 128 + 32 * s + 16 * h - mis;
+        const int os = tiled ? 3072 + 16 * (int)j + 8 * s : 192 + 8 * s - mis;
+        const int od = tiled ? 3328 + 2 * (int)j : 208;
         r.mis = (uint32_t)mis;
         r.a = mld16(blk + oa);
         r.b = mld16(blk + ob);
@@ -176,16 +168,18 @@ __device__ __forceinline__ typename MRawOf<T>::type mload(const uint8_t *row, co
         r.s2 = mld4(blk + os + (mis ? 8 : 4));
         r.d = *reinterpret_cast<const uint16_t *>(blk + od);
     } else if constexpr (T == T_FP8) {
-        const uint8_t *c = row + (int64_t)b * 256 + 32 * g;
-        r.a0 = mld16(c);
-        r.a1 = mld16(c + 16);
-        r.b0 = mld16(c + 128);
-        r.b1 = mld16(c + 144);
+        const uint8_t *c = base + (int64_t)b * 256;
+        const uint32_t o = off + 32 * (uint32_t)g;
+        r.a0 = mld16(c + o);
+        r.a1 = mld16(c + o + 16);
+        r.b0 = mld16(c + o + 128);
+        r.b1 = mld16(c + o + 144);
         r.sc = mld4(srow + (int64_t)b * 4);   // scale row of the lane's 128-row block
     } else {
-        const uint8_t *c = row + (int64_t)b * 128;
-        r.q0 = mld16(c + 32 * g);
-        r.q1 = mld16(c + 32 * g + 16);
+        const uint8_t *c = base + (int64_t)b * 128;
+        const uint32_t o = off + 32 * (uint32_t)g;
+        r.q0 = mld16(c + o);
+        r.q1 = mld16(c + o + 16);
         r.sc = mld4(srow + (int64_t)b * 16 + 4 * g);
     }
     (void)L;
@@ -285,12 +279,13 @@ __device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
     return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
 }
 
-// Half-group q of staged superblock cb, which is superblock cb0 + cb*stride of x
-// (AT: any launch-argument struct with x, n and k).
-template <int T, class AT>
-__device__ __forceinline__ void xhalf_fetch(const AT &A, int q, int cb0, int stride, XHalf &X) {
+// Half-group q (< 2^17) of staged superblock cb, which is superblock cb0 + cb*stride
+// of x.  r / n by a multiply with the launch's n-th reciprocal (exact for r < 2^16).
+template <int T>
+__device__ __forceinline__ void xhalf_fetch(const MmaArgs &A, int q, int cb0, int stride, XHalf &X) {
     const int n = A.n, h = q & 1, r = q >> 1;
-    const int t = n == 1 ? 0 : r % n, cg = n == 1 ? r : r / n, g = cg & 3, cb = cg >> 2;
+    const int cg = n == 1 ? r : (int)(((uint64_t)(uint32_t)r * A.nmagic) >> 32);
+    const int t = r - cg * n, g = cg & 3, cb = cg >> 2;
     const _Float16 *p = reinterpret_cast<const _Float16 *>(A.x) + (int64_t)t * A.k + (int64_t)(cb0 + cb * stride) * 256 +
                         xhalf_base<T>(g, h);
 #pragma unroll
@@ -338,8 +333,8 @@ __device__ __forceinline__ void xhalf_commit(int q, bool st, const XHalf &X, uin
 typedef KqSplit KqTile;
 
 template <bool Q5>
-__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, int g) {
-    return kq_split(R.hdr, kq_lane_consts(g), Q5 ? 31.0f : 15.0f);
+__device__ __forceinline__ KqTile kq_tile(const MRawKq &R, const KqLane &L) {
+    return kq_split(R.hdr, L, Q5 ? 31.0f : 15.0f);
 }
 
 template <bool Q5>
@@ -465,7 +460,7 @@ __device__ __forceinline__ void q6_dword(const MRawQ6 &R, const Q6Tile &K, const
 // One superblock of NT weight tiles for NG token groups.  xa[q] = the lane's nine
 // units of the superblock for token group q (or the zeros), read up front.
 template <int T, int NT, int NG, bool PAIRED = false>
-__device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int g, const uint4 *const (&xa)[NG],
+__device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int g, const KqLane &L, const uint4 *const (&xa)[NG],
                                     f4 (&acc)[NT][NG]) {
     const uint4 *const(&xv)[NG] = xa;   // LDS reads at their use; other waves hide the latency
     if constexpr (T == T_Q4_K || T == T_Q5_K) {
@@ -475,7 +470,7 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
         // r and X of sub-blocks 2g (first) and 2g+1 (second).
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            const KqTile K = kq_tile<T == T_Q5_K>(R[i], g);
+            const KqTile K = kq_tile<T == T_Q5_K>(R[i], L);
             f4 c1[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -593,7 +588,8 @@ __device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, in
 // not it has superblocks there, so all waves meet the same barriers.
 template <int T, int NT, int NG, int NP, int D>
 __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int sbs, int tl, bool dec, int g, int t,
-                                         const uint8_t *const (&wr)[NT], const uint8_t *const (&sr)[NT], uint4 *lds,
+                                         const uint8_t *const (&wr)[NT], const uint32_t (&wo)[NT],
+                                         const uint8_t *const (&sr)[NT], uint4 *lds,
                                          f4 (&acc)[NP][NT][NG]) {
     typedef typename MRawOf<T>::type Raw;
     // Ring depth D; unroll U, a multiple of D and of NP, so that ring slots and
@@ -603,8 +599,9 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
     const int n = A.n, nb = A.nb, kc = A.kc;
     const uint4 *zero = lds;   // kZeroUnits units of zeros
     uint4 *xu = lds + kZeroUnits;
-    const int cnt = kw < nb ? (nb - 1 - kw) / KW + 1 : 0;   // wave-uniform
-    const int maxcnt = (nb + KW - 1) / KW;                   // workgroup-uniform (the cnt of kw = 0)
+    const int lkw = __builtin_ctz((unsigned)KW);            // KW is a power of two
+    const int cnt = kw < nb ? ((nb - 1 - kw) >> lkw) + 1 : 0;   // wave-uniform
+    const int maxcnt = (nb + KW - 1) >> lkw;                     // workgroup-uniform (the cnt of kw = 0)
     auto sb = [&](int i) { return kw + i * KW; };
     const int lastb = cnt > 0 ? sb(cnt - 1) : nb - 1;
     const int nchunks = (nb + kc - 1) / kc;
@@ -613,11 +610,16 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
     // Lanes of tokens >= n read zeros (workgroup staging) or, in the decode path,
     // which meets no barrier after the zeros are written, the wave's own units:
     // their rows of the product are never stored.
+    const KqLane L = kq_lane_consts(g);   // K-quant scale-table selectors of the lane group
+    int lane_units[NG];   // the lane's (g, token) unit group, superblock 0
+#pragma unroll
+    for (int q = 0; q < NG; ++q) lane_units[q] = (g * n + 16 * q + t) * kUnitsPerTok;
     auto xa_of = [&](int cb, const uint4 *(&xa)[NG], const uint4 *other) {
+        const int cbo = cb * 4 * n * kUnitsPerTok;   // uniform
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
             const int tok = 16 * q + t;
-            xa[q] = tok < n ? xu + ((cb * 4 + g) * n + tok) * kUnitsPerTok : other;
+            xa[q] = tok < n ? xu + (lane_units[q] + cbo) : other;
         }
     };
 
@@ -646,7 +648,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
             const int q = q0 + lane;
             if (cnt > 0) xhalf_fetch<T>(A, q < hq ? q : hq - 1, kw, KW, X);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], sr[i], min(kw, lastb), g, sbs, tl);
+            for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], wo[i], sr[i], min(kw, lastb), g, sbs, tl);
             if (cnt > 0) xhalf_commit<T>(q, q < hq, X, xu);   // LDS order within a wave: no barrier
         }
 #pragma unroll
@@ -654,13 +656,17 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
             if (u + 1 < D) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], sr[i], min(sb(u + 1), lastb), g, sbs, tl);
+                for (int i = 0; i < NT; ++i) ring[u + 1][i] = mload<T>(wr[i], wo[i], sr[i], min(sb(u + 1), lastb), g, sbs, tl);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (u < cnt) {   // scalar branch
-                const uint4 *xa[NG];
-                xa_of(u, xa, xu);
-                msb<T, NT, NG>(ring[u], g, xa, acc[0]);
+                const uint4 *xa[NG];   // the lane's units, computed in place (fewer live registers)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    const int tok = 16 * q + t;
+                    xa[q] = tok < n ? xu + ((u * 4 + g) * n + tok) * kUnitsPerTok : xu;
+                }
+                msb<T, NT, NG>(ring[u], g, L, xa, acc[0]);
             }
         }
         return;
@@ -671,7 +677,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
 #pragma unroll
         for (int u = 0; u < D; ++u)
 #pragma unroll
-            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], sr[i], min(sb(u), lastb), g, sbs, tl);
+            for (int i = 0; i < NT; ++i) ring[u][i] = mload<T>(wr[i], wo[i], sr[i], min(sb(u), lastb), g, sbs, tl);
     });
     __syncthreads();
     int chunk = 0;
@@ -689,11 +695,11 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
                 }
                 const uint4 *xa[NG];
                 xa_of(b - chunk * kc, xa, zero);
-                msb<T, NT, NG>(ring[u % D], g, xa, acc[u % NP]);
+                msb<T, NT, NG>(ring[u % D], g, L, xa, acc[u % NP]);
             }
             if (it + D < cnt) {   // refill only with a superblock the wave still serves
 #pragma unroll
-                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], sr[i], min(sb(it + D), lastb), g, sbs, tl);
+                for (int i = 0; i < NT; ++i) ring[u % D][i] = mload<T>(wr[i], wo[i], sr[i], min(sb(it + D), lastb), g, sbs, tl);
             }
         }
     }
@@ -749,7 +755,8 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     const int n = A.n;
     if (threadIdx.x < kZeroUnits) lds[threadIdx.x] = make_uint4(0, 0, 0, 0);
 
-    const uint8_t *wr[NT];
+    const uint8_t *wr[NT];   // the wave's tile (uniform)
+    uint32_t wo[NT];         // the lane's offset from it
     const uint8_t *sr[NT];
     // K-quant superblock bytes; in the 16-row tiled layout a tile's chunks (16
     // superblocks each) follow one another from (r/16) * nb * 16 * sbytes.
@@ -758,9 +765,11 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t r = rows[i] < S.m ? rows[i] : S.m - 1;   // rows past m read row m-1; results dropped
+        // the tile's first row, clamped to the last tile (uniform): r - t0 is in 0..15
+        const int64_t t0 = min(rows[i] - (int64_t)j, (int64_t)(S.m - 1) & ~(int64_t)15);
         const bool second = up != 0;
-        const int64_t roff = S.tiled ? (r >> 4) * A.nb * 16 * sbytes : r * S.row_bytes;   // tiled: the tile's chunk 0
-        wr[i] = (second ? S.data2 : S.data) + roff;
+        wr[i] = (second ? S.data2 : S.data) + (S.tiled ? (t0 >> 4) * A.nb * 16 * sbytes : t0 * S.row_bytes);
+        wo[i] = S.tiled ? 0u : (uint32_t)((r - t0) * S.row_bytes);
         const uint8_t *sc = second ? S.scales2 : S.scales;
         // NVFP4: one e4m3 scale per 16 weights of the row; FP8: the bf16 scale row
         // of the row's 128-row block (K/128 scales of 2 bytes).
@@ -775,15 +784,15 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 #pragma unroll
             for (int q = 0; q < NG; ++q) ph[a][i][q] = (f4){0.f, 0.f, 0.f, 0.f};
     if ((TS & TS_Q4) && S.type == T_Q4_K)
-        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q4_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, wo, sr, lds, ph);
     else if ((TS & TS_Q5) && S.type == T_Q5_K)
-        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q5_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, wo, sr, lds, ph);
     else if ((TS & TS_Q6) && S.type == T_Q6_K)
-        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_Q6_K, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, wo, sr, lds, ph);
     else if ((TS & TS_F4) && S.type == T_NVFP4)
-        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_NVFP4, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, wo, sr, lds, ph);
     else if ((TS & TS_F8) && S.type == T_FP8)
-        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, sr, lds, ph);
+        mma_body<T_FP8, NT, NG, NP, D>(A, KW, kw, sbs, S.tiled, S.dec != 0, g, j, wr, wo, sr, lds, ph);
 
     // The KS phase partials of a row tile, added in phase order:
     //     y = (((p0 + p1) + p2) + ...) + p(KS-1).

@@ -48,6 +48,7 @@ struct MmaArgs {
     int32_t np;              // phases per wave (1, 2 or 4; divides every segment's ks): a row
                              // tile has kw = ks / np waves, wave w holding phases w, w + kw, ...
     int32_t xch;             // SwiGLU: 16-byte LDS unit where the gate sums are handed over
+    uint32_t nmagic;         // n >= 2: floor(2^32 / n) + 1, so r / n = umulhi(r, nmagic) for r < 2^16
 };
 
 // ts: bit set of the weight types in the launch (TS_Q4 | ...); grid: workgroups of

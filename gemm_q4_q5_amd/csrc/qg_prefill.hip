@@ -76,15 +76,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
 
     constexpr int S = T == T_Q4_K ? 144 : (T == T_Q5_K ? 176 : (T == T_Q6_K ? 210 : 0));
     const int sbs = A.tiled ? 16 * S : S;
-    const uint8_t *wr[NT];
+    const uint8_t *wr[NT];   // the wave's tile (uniform)
+    uint32_t wo[NT];         // the lane's offset from it
     const uint8_t *sr[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t r = r0 + 16 * i + j, rc = r < A.m ? r : A.m - 1;
-        wr[i] = A.tiled ? A.data + (rc >> 4) * (int64_t)nb * 16 * S : A.data + rc * A.row_bytes;
+        const int64_t t0 = min(r0 + 16 * i, (A.m - 1) & ~(int64_t)15);   // uniform; rc - t0 in 0..15
+        wr[i] = A.tiled ? A.data + (t0 >> 4) * (int64_t)nb * 16 * S : A.data + t0 * A.row_bytes;
+        wo[i] = A.tiled ? 0u : (uint32_t)((rc - t0) * A.row_bytes);
         sr[i] = T == T_NVFP4 ? A.scales + rc * (A.row_bytes / 8)
                              : (T == T_FP8 ? A.scales + (rc >> 7) * (A.row_bytes / 64) : nullptr);
     }
+    const KqLane L = kq_lane_consts(g);
     const _Float16 *xsrc[HPT];
 #pragma unroll
     for (int v = 0; v < HPT; ++v) xsrc[v] = p_xsrc<T, BM>(A, t0, tid + 256 * v);
@@ -101,11 +105,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
         const uint4 *xa[NG];
 #pragma unroll
         for (int q = 0; q < NG; ++q) xa[q] = xl + 16 * q * kUnitsPerTok;
-        msb<T, NT, NG, true>(R, g, xa, acc);
+        msb<T, NT, NG, true>(R, g, L, xa, acc);
     };
     auto load_w = [&](Raw (&R)[NT], int b) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) R[i] = mload<T>(wr[i], sr[i], b, g, sbs, A.tiled);
+        for (int i = 0; i < NT; ++i) R[i] = mload<T>(wr[i], wo[i], sr[i], b, g, sbs, A.tiled);
     };
     // x of superblock b: loads into registers, then (after a barrier) into LDS.
     auto fetch_x = [&](XHalf (&X)[HPT], int b) __attribute__((always_inline)) {
