@@ -4,7 +4,7 @@
 // Reference: reflex-llm Performance page, Path E / E5 -- a tensor-core K-quant
 // prefill GEMM whose per-(row, sub-block) scales are decoded once and whose
 // dequantized weights serve many tokens.  Here a workgroup owns a block of 16*NG
-// tokens by 64*NT weight rows.  Each of its four waves owns NT row tiles (16 rows
+// tokens by 16*WV*NT weight rows.  Each of its WV waves owns NT row tiles (16 rows
 // each) and builds their v_mfma_f32_16x16x32_f16 weight operands in its own
 // registers, straight from the streamed superblocks (the same loads and unpacking
 // as the 1..32-token product), so a weight is decoded once per token block and
@@ -57,11 +57,11 @@ __device__ __forceinline__ void p_xcommit(int q, const XHalf &X, uint4 *xs) {
     }
 }
 
-template <int T, int NT, int NG>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
-    constexpr int BM = 16 * NG, BN = 64 * NT;
-    constexpr int HPT = 8 * BM / 256;   // x half-groups per thread and superblock
-    static_assert(HPT >= 1 && (8 * BM) % 256 == 0, "token block too small");
+template <int T, int NT, int NG, int WV>
+__global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A) {
+    constexpr int BM = 16 * NG, BN = 16 * WV * NT, NTH = 64 * WV;
+    constexpr int HPT = 8 * BM / NTH;   // x half-groups per thread and superblock
+    static_assert(HPT >= 1 && (8 * BM) % NTH == 0, "token block too small");
     typedef typename MRawOf<T>::type Raw;
     extern __shared__ uint4 lds[];   // the block's x for one superblock: 4 * BM * 9 units
 
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
     const KqLane L = kq_lane_consts(g);
     const _Float16 *xsrc[HPT];
 #pragma unroll
-    for (int v = 0; v < HPT; ++v) xsrc[v] = p_xsrc<T, BM>(A, t0, tid + 256 * v);
+    for (int v = 0; v < HPT; ++v) xsrc[v] = p_xsrc<T, BM>(A, t0, tid + NTH * v);
 
     f4 acc[NT][NG];
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
     };
     auto commit_x = [&](const XHalf (&X)[HPT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < HPT; ++v) p_xcommit<T>(tid + 256 * v, X[v], lds);
+        for (int v = 0; v < HPT; ++v) p_xcommit<T>(tid + NTH * v, X[v], lds);
     };
 
     // Per superblock b: b+1's weights and x go out, b is computed, barrier, b+1's x
@@ -136,21 +136,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
     fetch_x(X, 0);
     commit_x(X);
     __syncthreads();
-    // Two superblocks per trip so that the ring slots are compile-time.
+    // Two superblocks per trip so that the ring slots are compile-time.  The loads are
+    // unconditional (the superblock index clamped to the last one; a redundant load at
+    // the end): loads under a branch make the compiler wait for them at the join.  The
+    // scheduling barriers keep them ahead of the computation (left alone, the compiler
+    // sinks them to its end, which exposes their whole latency).
     for (int b = 0; b < nb; b += 2) {
-        if (b + 1 < nb) {
-            load_w(ring1, b + 1);
-            fetch_x(X, b + 1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ring1, min(b + 1, nb - 1));
+        fetch_x(X, min(b + 1, nb - 1));
+        __builtin_amdgcn_sched_barrier(0);
         compute(ring0);
         __syncthreads();
         if (b + 1 >= nb) break;   // uniform
         commit_x(X);
         __syncthreads();
-        if (b + 2 < nb) {
-            load_w(ring0, b + 2);
-            fetch_x(X, b + 2);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ring0, min(b + 2, nb - 1));
+        fetch_x(X, min(b + 2, nb - 1));
+        __builtin_amdgcn_sched_barrier(0);
         compute(ring1);
         __syncthreads();
         if (b + 2 >= nb) break;
@@ -172,34 +176,36 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs A) {
     }
 }
 
-template <int T, int NT, int NG>
+template <int T, int NT, int NG, int WV>
 static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
-    constexpr int BM = 16 * NG, BN = 64 * NT;
+    constexpr int BM = 16 * NG, BN = 16 * WV * NT;
     const int64_t blocks = (A.m + BN - 1) / BN * ((A.n + BM - 1) / BM);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)4 * BM * kUnitsPerTok * 16;
-    const void *fn = (const void *)prefill_kernel<T, NT, NG>;
+    const void *fn = (const void *)prefill_kernel<T, NT, NG, WV>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_kernel<T, NT, NG>), dim3((unsigned)blocks), dim3(256), lds, st, A);
+    hipLaunchKernelGGL((prefill_kernel<T, NT, NG, WV>), dim3((unsigned)blocks), dim3(64 * WV), lds, st, A);
     return hipGetLastError();
 }
 
-// 64 tokens x 64 weight rows per workgroup (one row tile per wave, four token
-// groups).  Measured at 512 tokens against 128 x 128, 128 x 64 and 64 x 128 blocks of
-// the same kernel (Q4_K 9728x2560 / Q6_K 2560x9728 / Q5_K 4096x2560, µs): 64.6 /
-// 102.8 / 35.5 against 66.8 / 139.0 / 38.5 (64 x 128) and 82.0 / 134.0 / 40.0
-// (128 x 64): the small block keeps up to three workgroups per CU busy (at most 160
-// VGPRs, 37 KB of LDS), and the larger ones spill registers or leave CUs idle.
+// 64 tokens per workgroup, one 16-row tile per wave and four token groups: 128 weight
+// rows in eight waves for the K-quants, 64 rows in four for FP8 and NVFP4.  Measured
+// at 512 tokens (Q4_K 9728x2560 / Q6_K 2560x9728 / Q5_K 4096x2560, µs): eight waves
+// 61.0 / 88.0 / 31.1 against 62.2 / 89.4 / 33.8 with four (each wave's work is the
+// same; a block's x is staged by twice the threads, so each holds half as much of it
+// in registers); 128 tokens in eight waves 87.4 / 145.7 / 46.8; 32 tokens in four
+// 64.5 / 97.8 / 38.9; earlier, two tiles per wave (64 x 128 in four waves) or 128
+// tokens in four waves spilled registers or left CUs idle.
 hipError_t launch_prefill(const PrefillArgs &A, hipStream_t st) {
     switch (A.type) {
-    case T_Q4_K: return launch_cfg<T_Q4_K, 1, 4>(A, st);
-    case T_Q5_K: return launch_cfg<T_Q5_K, 1, 4>(A, st);
-    case T_Q6_K: return launch_cfg<T_Q6_K, 1, 4>(A, st);
-    case T_FP8: return launch_cfg<T_FP8, 1, 4>(A, st);
-    default: return launch_cfg<T_NVFP4, 1, 4>(A, st);
+    case T_Q4_K: return launch_cfg<T_Q4_K, 1, 4, 8>(A, st);
+    case T_Q5_K: return launch_cfg<T_Q5_K, 1, 4, 8>(A, st);
+    case T_Q6_K: return launch_cfg<T_Q6_K, 1, 4, 8>(A, st);
+    case T_FP8: return launch_cfg<T_FP8, 1, 4, 4>(A, st);
+    default: return launch_cfg<T_NVFP4, 1, 4, 4>(A, st);
     }
 }
 
