@@ -12,12 +12,12 @@
 //   Q6_K 210 B: 128 B low nibbles, 64 B high 2-bit pairs, 16 int8 scales, fp16 d.
 //   NVFP4:      e2m1 codes (low nibble = even element), e4m3 scale per 16.
 //
-// Unpacking (gfx950): quants become fp16 by OR-ing them into the mantissa of an
-// fp16 constant, two weights per VALU op.  The dequant probe and the prefill's fp16
-// tile use the normal-range "magic" form (low nibble q -> 1024 + q, high nibble
-// q -> 256 + 4q, recovered exactly by one subtraction); the decode product feeds the
-// quant as an fp16 subnormal (q * 2^-24 or q * 2^-20) straight into a mixed-precision
-// fma.  Q6_K centres q at 32: (1024 + q) - 1056 or (256 + 4q) - 384 per group.
+// Unpacking (gfx950): two weights per VALU op.  The dequant probe ORs quants into
+// the mantissa of an fp16 constant (the normal-range "magic" form: low nibble
+// q -> 1024 + q, high nibble q -> 256 + 4q, recovered exactly by one subtraction;
+// Q6_K centres q at 32: (1024 + q) - 1056 or (256 + 4q) - 384 per group).  The
+// products (1..32 tokens and prefill) mask the quant in place as an fp16 subnormal
+// (q * 2^-24 or q * 2^-20) and scale it with one packed fp16 fma per two weights.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,18 +37,6 @@ __device__ __forceinline__ float f16lo(uint32_t u) {
 __device__ __forceinline__ float f16hi(uint32_t u) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
 }
-
-// Q4_K / Q5_K superblock: U with |w| < 2^U for every weight of the superblock, from
-// dd = d | dmin << 16 alone.  With Ed, Em the fp16 exponent fields (0 for subnormals),
-// d < 2^(Ed-14) and dmin < 2^(Em-14); sc*q <= 63*31 < 2^11 and m <= 63 < 2^6, and
-// |d*sc*q - dmin*m| <= max(d*sc*q, dmin*m).  Range -8..27.
-__device__ __forceinline__ int kq_exp_bound(uint32_t dd) {
-    const int ed = (int)((dd >> 10) & 31u), em = (int)((dd >> 26) & 31u);
-    return max(ed - 3, em - 8);
-}
-
-// Q6_K superblock: |d*sc*(q-32)| < 2^(Ed-2) (|sc| <= 128 = 2^7, |q-32| <= 32 = 2^5).
-__device__ __forceinline__ int q6_exp_bound(uint32_t dbits) { return (int)((dbits >> 10) & 31u) - 2; }
 
 // (a & m) | o in one VALU op.  VOP3 on gfx9 takes no literal operands, so the
 // compiler splits the literal-mask form into v_and + v_or; with the mask in an
@@ -127,35 +115,6 @@ __device__ __forceinline__ KqCoef kq_coef(uint4 hdr, const KqLane &L) {
     return k;
 }
 
-// 2^e as fp32 (e in -126..127).
-__device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23); }
-
-// Scaled coefficients of the lane's two sub-blocks for fp16 weight operands: with U =
-// kq_exp_bound(d | dmin << 16), a weight whose quant q sits in the mantissa of an fp16
-// subnormal (q * 2^-24 for the low sub-block, q * 2^-20 for the high one, Q5_K's fifth
-// bit included) becomes  fp16(a * v + b) = fp16((d*sc*q - dmin*m) * 2^(15-U))  in one
-// mixed-precision fma (mix2): a*v + b is exact in fp32, |result| < 2^15.
-struct KqScaled {
-    float a0, b0, a1, b1;
-    int u;
-};
-
-// u: the exponent to scale by, at least kq_exp_bound(hdr.x) (the decode product passes
-// exactly that; the prefill a running maximum over the row's superblocks, <= 27).
-__device__ __forceinline__ KqScaled kq_scaled(uint4 hdr, const KqLane &L, int u) {
-    uint32_t sc, mn;
-    kq_scale_min(hdr, L, sc, mn);
-    KqScaled k;
-    k.u = u;
-    const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
-    const float dm = -dmin * pow2f(15 - k.u);          // exact: power-of-two scaling in range
-    k.a0 = d * pow2f(39 - k.u) * (float)(sc & 0xFFu);  // <= 17 significant bits: exact
-    k.a1 = d * pow2f(35 - k.u) * (float)((sc >> 8) & 0xFFu);
-    k.b0 = dm * (float)(mn & 0xFFu);
-    k.b1 = dm * (float)((mn >> 8) & 0xFFu);
-    return k;
-}
-
 // Exact split of the lane's two sub-blocks of a Q4_K / Q5_K superblock for the matrix
 // cores.  With A = d*sc and B = dmin*m (both exact in fp32) and an integer c in
 // [0, qmax] (the nearest to B/A, 0 when A = 0), every weight of the sub-block is
@@ -218,15 +177,6 @@ __device__ __forceinline__ float hsum16(uint4 a, uint4 b) {
     s = __builtin_amdgcn_fdot2(as_h2(b.z), one, s, false);
     s = __builtin_amdgcn_fdot2(as_h2(b.w), one, s, false);
     return s;
-}
-
-// fp16(a*v + b) for the two fp16 halves of v, one rounding each
-// (v_fma_mixlo_f16 / v_fma_mixhi_f16).
-__device__ __forceinline__ uint32_t mix2(uint32_t v, float a, float b) {
-    const h2 h = as_h2(v);
-    const _Float16 lo = (_Float16)__builtin_fmaf(a, (float)h.x, b);
-    const _Float16 hi = (_Float16)__builtin_fmaf(a, (float)h.y, b);
-    return as_u32((h2){lo, hi});
 }
 
 // The Q5_K fifth bits of four positions, OR-ed into the subnormal quant pairs of one

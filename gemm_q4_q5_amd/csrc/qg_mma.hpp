@@ -30,21 +30,21 @@
 // pipeline is full, and a workgroup barrier after the loads, or x staged by some
 // waves for all, held whole workgroups until their slowest wave had its data.
 //
-// Exact operands.  Q4_K/Q5_K: the weight operand is the weight itself, rounded once
-// to fp16 at a power-of-two scale of its (row, superblock):
-//     w' = fp16((d*sc*q - dmin*m) * 2^(15-U)),   y += 2^(U-15) * sum_k w'*x
-// with U = max(Ed - 3, Em - 8) from the fp16 exponent fields Ed, Em of d and dmin, so
-// |w| < 2^U and |w'| < 2^15 (no overflow), and every weight of magnitude at least
-// 2^(U-29) is an fp16 normal (relative error <= 2^-11 of |w| itself).  A weight that
-// is exactly zero stays exactly zero, and the error of a row scales with
-// sum|w||x|, not with the sizes of the two terms that cancel in it.  The quant
-// enters the mixed-precision fma as an fp16 subnormal (its bits in the low mantissa),
-// so a*q + b is formed exactly in fp32 and rounded once.
-// Q6_K: the operand is sc*(q-32), exact whenever |sc*(q-32)| <= 2048 (every
-// |sc| <= 64, which covers int8 scales drawn in 0..63), otherwise rounded once to
-// fp16 (relative error <= 2^-11); d is applied in fp32.  NVFP4: e2m1 * e4m3 is exact
-// in fp16 and the MFMA accumulates over all of K.  FP8: the code is exact in fp16
-// and the bf16 block scale is applied in fp32 per 128-wide block.
+// Exact operands.  Q4_K/Q5_K: each weight w = A*q - B of a sub-block (A = d*sc,
+// B = dmin*m, exact in fp32) is split as w = d*2^14*o + r with c = the integer in
+// [0, qmax] nearest B/A (0 where A = 0), the fp16 operand o = (q - c)*sc*2^-14 (exact:
+// |q - c|*sc < 2^11) and the per-sub-block remainder r = A*c - B (one fp32 rounding,
+// |r| <= |w| for every q of the sub-block).  A superblock's MFMA chain over o is
+// scaled by d*2^14 in fp32, and two fp32 MFMAs add r times the sub-block sums of x.
+// Nothing subtracts two large rounded sums, so the error of a row scales with
+// sum|w||x|, and a sub-block whose weights are all zero (A*q = B) contributes
+// exactly zero.  The quant enters one packed fp16 fma per two weights as an fp16
+// subnormal (its bits in the low mantissa), so o is formed without any rounding.
+// Q6_K: the operand is (q-32)*sc*2^-16, exact for |sc| <= 64 (int8 scales drawn in
+// 0..63), otherwise rounded once to fp16 (relative error <= 2^-11); d*2^16 is applied
+// in fp32.  NVFP4: e2m1 * e4m3 is exact in fp16 and the MFMA accumulates over all of
+// K.  FP8: the code is exact in fp16 and the bf16 block scale is applied in fp32 per
+// 128-wide block.
 //
 // Row invariance.  An output (t, r) is produced by the same instructions for every
 // n: its MFMAs see only token t's x (A row t) and row r's weights (B column r);
