@@ -106,6 +106,9 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
 #pragma unroll
         for (int q = 0; q < NG; ++q) xa[q] = xl + 16 * q * kUnitsPerTok;
         msb<T, NT, NG, true>(R, g, L, xa, acc);
+        // The compiler's interleaving of the MFMAs with the operand construction and
+        // the x reads (mode 1): 3-4 % faster at 512 tokens than its default order.
+        __builtin_amdgcn_iglp_opt(1);
     };
     auto load_w = [&](Raw (&R)[NT], int b) __attribute__((always_inline)) {
 #pragma unroll
