@@ -337,9 +337,9 @@ PREFILL_N = 512
 PREFILL_COPIES = 4
 
 
-def time_prefill(reps=10):
-    """Prefill chunk of 512 tokens through the MFMA GEMM on the three config
-    shapes (4 rotated copies of each weight), from a HIP graph."""
+def _prefill_calls():
+    """calls(only=None): the prefill calls on the three shapes, each over its rotated copies
+    (only = an index into PREFILL for one shape)."""
     import torch
     import gemm_q4_q5_amd as qg
     import synth
@@ -358,6 +358,34 @@ def time_prefill(reps=10):
                 if only is None or only == i:
                     qg.qgemm_prefill(ws[i][c], xs[k], ys[i])
 
+    return calls
+
+
+def replay_prefill(name, steps, warmup):
+    """Profile mode: one prefill shape's graph (its rotated copies), `steps` launches after
+    `warmup`; one JSON line."""
+    import torch
+    only = [p[0] for p in PREFILL].index(name)
+    calls = _prefill_calls()
+    calls(only)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(only)
+    reps = max(1, steps // PREFILL_COPIES)
+    ms = _time_graph(g, reps, max(1, warmup // PREFILL_COPIES))
+    us = 1000.0 * ms / (reps * PREFILL_COPIES)
+    _, _, m, k = PREFILL[only]
+    print(json.dumps({"prefill_call": name, "tokens": PREFILL_N, "launches": reps * PREFILL_COPIES,
+                      "us_per_launch": round(us, 2),
+                      "TFLOP/s": round(2.0 * PREFILL_N * m * k / (us * 1e-6) / 1e12, 1)}))
+
+
+def time_prefill(reps=10):
+    """Prefill chunk of 512 tokens through the MFMA GEMM on the three config
+    shapes (4 rotated copies of each weight), from a HIP graph."""
+    import torch
+    calls = _prefill_calls()
     calls()
     torch.cuda.synchronize()
     out = {}
@@ -541,6 +569,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=1, help="tokens per call in --kernel mode")
     ap.add_argument("--calibrate", action="store_true",
                     help="--kernel mode: also run the known-size copy that scales HBM counters")
+    ap.add_argument("--prefill-call", choices=[p[0] for p in PREFILL], default=None,
+                    help="profile mode: replay only this prefill call (its rotated copies)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two counter runs of --kernel K into profiles/traffic_K.json")
     args = ap.parse_args()
@@ -556,6 +586,9 @@ def main():
     import gemm_q4_q5_amd as qg
     qg.lib()   # fails loudly if the HIP library is not built
     torch.cuda.set_device(0)
+    if args.prefill_call:
+        replay_prefill(args.prefill_call, args.steps, args.warmup)
+        return
 
     layers = build_layers(LAYERS, layout=args.layout)
     if args.kernel:
