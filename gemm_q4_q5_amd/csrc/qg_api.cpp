@@ -205,14 +205,16 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     } else {
         // From 8 tokens on x staging sets the pace: the largest grid of at most one
         // workgroup per CU, preferring (on equal grids) two phases per wave, then
-        // 16-wave workgroups.  Without such a grid (large matrices), the most phases
+        // 16-wave workgroups (10-wave ones where they give a larger grid).  Without such a grid (large matrices), the most phases
         // per wave and 8-wave workgroups.  Measured at 8 / 16 / 32 tokens (cold rotations, us):
         // the gate/up pair 15.4 -> 13.4 / 15.9 -> 14.4 / 21.0 -> 19.3 (two phases,
         // 16 waves, 152 workgroups) against the next best choices; the Q6_K down
         // 2560x9728 keeps 160 workgroups of 8 waves with two phases (26.9 at 32
         // tokens, 27.9 with 16 waves and one phase), Wo 2560x4096 160 of 8 with one
         // (11.9; 14.3 with two).
-        static const int kPref[7][2] = {{16, 2}, {8, 2}, {16, 4}, {8, 4}, {16, 1}, {8, 1}, {4, 1}};
+        // Ten-wave workgroups (five tiles of two phases, plain launches) fill more CUs
+        // where the tiles do not divide evenly into 8 or 16 per workgroup.
+        static const int kPref[8][2] = {{16, 2}, {10, 2}, {8, 2}, {16, 4}, {8, 4}, {16, 1}, {8, 1}, {4, 1}};
         bool dec4 = true;   // every matrix takes the decode path in 4-wave workgroups
         for (int s = 0; s < a.nseg; ++s) dec4 = dec4 && dec_ok(s, 4);
         int best = 0;
@@ -220,6 +222,11 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
             const int cw = c[0], p = c[1];
             if (p > np_max || p < np_min || ksmin < p || pair * ksmax / p > cw || (sw && cw < 8) || (cw == 4 && !dec4))
                 continue;
+            if (cw == 10) {   // every matrix's waves per tile must divide the workgroup; plain only
+                bool fits = !sw;
+                for (int s = 0; s < a.nseg; ++s) fits = fits && cw % (ks[s] / p) == 0;
+                if (!fits) continue;
+            }
             const int gr = grid_for(cw, p);
             if (gr <= kCUs && gr > best) {
                 best = gr;

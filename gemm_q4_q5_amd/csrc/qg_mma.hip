@@ -7,6 +7,7 @@ hipError_t launch_mma(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_
     switch (A.wv) {
     case 4: return launch_mma_w4(A, ts, grid, lds, st);
     case 8: return launch_mma_w8(A, ts, grid, lds, st);
+    case 10: return launch_mma_w10(A, ts, grid, lds, st);
     case 16: return launch_mma_w16(A, ts, grid, lds, st);
     default: return hipErrorInvalidValue;
     }

@@ -42,7 +42,8 @@ struct MmaArgs {
     int32_t nb;              // k / 256
     int32_t n;               // tokens, 1..32
     int32_t kc;              // superblocks per staged x chunk
-    int32_t wv;              // waves per workgroup (4, 8 or 16; 8 or 16 when np > 1 or for SwiGLU)
+    int32_t wv;              // waves per workgroup (4, 8, 10 or 16; 8 or 16 when np > 1 or for SwiGLU,
+                             // 10 only with np = 2 in plain launches)
     int32_t nt;              // weight tiles per wave (1)
     int32_t mode;            // MODE_PLAIN or MODE_SWIGLU
     int32_t np;              // phases per wave (1, 2 or 4; divides every segment's ks): a row
@@ -58,5 +59,6 @@ hipError_t launch_mma(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_
 hipError_t launch_mma_w4(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
 hipError_t launch_mma_w8(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
 hipError_t launch_mma_w16(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);
+hipError_t launch_mma_w10(const MmaArgs &A, int ts, int grid, size_t lds, hipStream_t st);   // np = 2, plain
 
 }  // namespace qg
