@@ -69,9 +69,11 @@
  *  - Accuracy: a Q4_K / Q5_K weight enters the product exactly, split as
  *    d*sc*(q - c) + r with c the integer nearest to dmin*m/(d*sc) (an exact fp16
  *    operand times d, and a per-sub-block fp32 remainder r times the sub-block's
- *    sum of x), both parts bounded by the weight; Q6_K, FP8 and NVFP4 weights
- *    enter as the exact weight times a power of two, rounded once to fp16
- *    (relative error <= 2^-11 wherever the scaled weight is an fp16 normal).
+ *    sum of x), both parts bounded by the weight; a Q6_K weight enters as the fp16
+ *    operand (q - 32)*sc*2^-16 times d*2^16, exact for |sc| <= 64 and otherwise
+ *    rounded once (relative error <= 2^-11); FP8 and NVFP4 weights enter exactly
+ *    (the e4m3 code, or e2m1 times its e4m3 scale, is exact in fp16, and the
+ *    block scales are applied in fp32).
  *    With fp32 accumulation |y - y_exact| stays within 2e-3 * sum_k |w||x| also
  *    where the two terms of a Q4_K / Q5_K weight cancel, and an output whose
  *    weights are all zero is exactly zero (exactly resid for qgemv_add).
@@ -215,10 +217,9 @@ int qgemv_pair_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
  * prefill GEMM with scales decoded once per (row, sub-block) and one dequantized
  * weight tile shared by all waves of a block): Y[n][m] = X[n][k] W^T for any
  * n >= 1 and every weight type.  Each wave decodes the weights of its 16 rows
- * once per 64 tokens into MFMA operands in registers (Q4_K / Q5_K: the exact split
- * described under Accuracy; the others: the exact weight times a power of two of
- * its row, rounded once to fp16, the row's sums scaled back exactly when stored)
- * and multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
+ * once per 64 tokens into MFMA operands in registers (the operands and per-
+ * superblock arithmetic of the 1..32-token calls, described under Accuracy) and
+ * multiplies with v_mfma_f32_16x16x32_f16, fp32 accumulation.  x fp16 [n][k],
  * y fp32 [n][m].  n up to 2^30; QG_ERR_SHAPE if the call would need more than
  * 2^31 - 1 blocks of Y (64 x 64 each).  Deterministic; no row-invariance
  * contract ([TK] "Prefill kernels": chunk kernels share work across rows and are
