@@ -143,13 +143,16 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
     const int ng = n > 16 ? 2 : 1;
     const size_t per_sb = (size_t)n * kMmaBytesPerTokSb;
     // Decode path (each wave stages its own x, one phase per wave) where a wave's
-    // superblocks fit one round of loads and their x one staging half-group per lane.
+    // superblocks fit one round of loads and their x (16 items of 32 bytes per
+    // superblock and token) kMmaDecRounds rounds of two items per lane.
     const int depth = qg::kMmaDepth;
     auto dec_ok = [&](int s, int wv) {
         const int maxcnt = (a.nb + ks[s] - 1) / ks[s];
         const size_t need = kMmaZeroBytes + (size_t)wv * maxcnt * per_sb;
-        return maxcnt <= depth && 8 * n * maxcnt <= 64 * qg::kMmaDecRounds && need <= kMmaLdsBudget;
+        return maxcnt <= depth && 16 * n * maxcnt <= 128 * qg::kMmaDecRounds && need <= kMmaLdsBudget;
     };
+    bool has_q6 = false;
+    for (int s = 0; s < nseg; ++s) has_q6 = has_q6 || w[s]->type == QG_Q6_K;
     bool one_type = true;
     for (int s = 1; s < nseg; ++s) one_type = one_type && w[s]->type == w[0]->type;
     // Several phases per wave take one weight type per launch.
@@ -222,6 +225,7 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
             const int cw = c[0], p = c[1];
             if (p > np_max || p < np_min || ksmin < p || pair * ksmax / p > cw || (sw && cw < 8) || (cw == 4 && !dec4))
                 continue;
+            if (cw == 16 && p == 4 && ng == 2 && has_q6) continue;   // not instantiated (registers)
             if (cw == 10) {   // every matrix's waves per tile must divide the workgroup; plain only
                 bool fits = !sw;
                 for (int s = 0; s < a.nseg; ++s) fits = fits && cw % (ks[s] / p) == 0;

@@ -210,16 +210,20 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_m
 // branch, no exec mask).
 //
 // k-slot order of step s for lane group g (offsets inside the superblock):
-//   Q4_K/Q5_K: 64g + {4s, 4s+2, 4s+1, 4s+3, 32+4s, 34+4s, 33+4s, 35+4s}
+//   Q4_K:      64g + 8s + {0, 2, 1, 3, 4, 6, 5, 7}   (steps 0..3: sub-block 2g,
+//              4..7: sub-block 2g+1)
+//   Q5_K:      64g + {4s, 4s+2, 4s+1, 4s+3, 32+4s, 34+4s, 33+4s, 35+4s}
 //   Q6_K:      128(g >> 1) + 16(g & 1) + 4(s >> 1) + 64(s & 1) + {0..3, 32..35}
 //   NVFP4:     64g + 8s + 0..7
 //   FP8:       128(s >> 2) + 32g + 8(s & 3) + 0..7   (steps 0..3 and 4..7 each stay
 //              inside one 128-wide scale block)
+// (The prefill GEMM stages its own x, in the orders of pkq_step and q6_dword.)
 constexpr int kUnitsPerTok = 9;
 constexpr int kZeroUnits = 9;
 // Q4_K / Q5_K: the ninth unit of (cb, g, t) holds the fp32 sums of x over the lane
 // group's two sub-blocks, half by half: {sum over positions 0..15 of sub-block 2g,
-// of 2g+1, over positions 16..31 of 2g, of 2g+1} (see xhalf_commit).
+// of 2g+1, over positions 16..31 of 2g, of 2g+1} (hsum16 of the two pieces; see
+// xp_commit).
 constexpr int kXSumUnit = 8;
 
 template <int T>
@@ -239,9 +243,8 @@ __device__ __forceinline__ void slot_pieces(int g, int s, int &o0, int &o1) {
     }
 }
 
-// A staging half-group: the x behind units 4h .. 4h+3 of one (superblock, lane
-// group, token), fetched as four 16-byte loads from one base; half-group index
-// q = ((cb*4 + g)*n + t)*2 + h.
+// The prefill's staging half-group: the x behind units 4h .. 4h+3 of one
+// (superblock, lane group, token), fetched as four 16-byte loads from one base.
 struct XHalf {
     uint4 v[4];
 };
@@ -279,57 +282,137 @@ __device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
     return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
 }
 
-// Half-group q (< 2^17) of staged superblock cb, which is superblock cb0 + cb*stride
-// of x.  r / n by a multiply with the launch's n-th reciprocal (exact for r < 2^16).
+// Staging by items of 32 bytes.  Lane groups 2gh and 2gh+1 of (staged superblock
+// cb, token t) take 256 bytes of x (one run; FP8: two 128-byte lines), eight items
+// of two 16-byte pieces each; item i has r2 = i >> 3 = (cb*2 + gh)*n + t and k =
+// i & 7, which names its lane group 2gh + xp_ge(k) and its pieces 2jp, 2jp+1 (jp =
+// xp_jp(k)) of that group's eight, piece j the x behind unit j (see xp_commit).
+// Consecutive lanes take consecutive items, so each quad of lanes in a load reads
+// one whole 128-byte line.  (Lanes that fetched the four loads of half a unit group
+// touched two lines per quad: the 32-token calls staged x 15-20 % slower, the
+// lines' lookups and not their bytes setting the pace.)  A lane's items are i0 +
+// u*STEP for its passes u; STEP is a multiple of 8, so the lane's k is fixed and its
+// r2 advances by the uniform STEP/8, carried over n by XPos.
+
+// Byte offsets of item k inside its record pair's x, and of the record pair gh
+// inside the superblock's 512 bytes.
 template <int T>
-__device__ __forceinline__ void xhalf_fetch(const MmaArgs &A, int q, int cb0, int stride, XHalf &X) {
-    const int n = A.n, h = q & 1, r = q >> 1;
-    const int cg = n == 1 ? r : (int)(((uint64_t)(uint32_t)r * A.nmagic) >> 32);
-    const int t = r - cg * n, g = cg & 3, cb = cg >> 2;
-    const _Float16 *p = reinterpret_cast<const _Float16 *>(A.x) + (int64_t)t * A.k + (int64_t)(cb0 + cb * stride) * 256 +
-                        xhalf_base<T>(g, h);
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(p + xhalf_off<T>(l));
-        X.v[l] = make_uint4(v.x, v.y, v.z, v.w);
-    }
+__device__ __forceinline__ uint32_t xp_koff(int k) {
+    if constexpr (T == T_FP8) return 256u * (uint32_t)(k >> 2) + 32u * (uint32_t)(k & 3);
+    else return 32u * (uint32_t)k;
+}
+template <int T>
+__device__ __forceinline__ uint32_t xp_gbase(int gh) {
+    return (T == T_FP8 ? 128u : 256u) * (uint32_t)gh;
+}
+template <int T>
+__device__ __forceinline__ int xp_ge(int k) {
+    if constexpr (T == T_Q6_K) return k & 1;
+    else if constexpr (T == T_FP8) return (k >> 1) & 1;
+    else return k >> 2;
+}
+template <int T>
+__device__ __forceinline__ int xp_jp(int k) {
+    if constexpr (T == T_Q6_K) return k >> 1;
+    else if constexpr (T == T_FP8) return 2 * (k >> 2) + (k & 1);
+    else return k & 3;
 }
 
-// Writes the half-group's four units (if `st`: the lane's half-group exists).
+// r2 = cg*n + t (cg = cb*2 + gh).
+struct XPos {
+    int t, cg;
+};
+// r / n by a multiply with the launch's n-th reciprocal (exact for r < 2^16).
+__device__ __forceinline__ XPos xpos_of(const MmaArgs &A, int r) {
+    const int cg = A.n == 1 ? r : (int)(((uint64_t)(uint32_t)r * A.nmagic) >> 32);
+    return {r - cg * A.n, cg};
+}
+// r2 + d for d = dcg*n + dt, 0 <= dt < n.
+__device__ __forceinline__ XPos xpos_step(XPos p, int n, int dt, int dcg) {
+    int t = p.t + dt, cg = p.cg + dcg;
+    const bool wrap = t >= n;
+    t = wrap ? t - n : t;
+    cg = wrap ? cg + 1 : cg;
+    return {t, cg};
+}
+// Item (p, k) of staged superblocks cb0 + cb*stride, its two pieces; cg is clamped to
+// cgmax (items past the end re-read the last record pair and are not written).
 template <int T>
-__device__ __forceinline__ void xhalf_commit(int q, bool st, const XHalf &X, uint4 *xs) {
-    uint4 *u = xs + (q >> 1) * kUnitsPerTok + 4 * (q & 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint2 p0 = xhalf_piece<T>(X, i, 0), p1 = xhalf_piece<T>(X, i, 1);
-        uint4 v;
-        if constexpr (T == T_Q4_K || T == T_Q5_K) {
-            // [x0 x1 x2 x3] -> [x0 x2] [x1 x3]
-            v.x = __builtin_amdgcn_perm(p0.y, p0.x, 0x05040100u);
-            v.y = __builtin_amdgcn_perm(p0.y, p0.x, 0x07060302u);
-            v.z = __builtin_amdgcn_perm(p1.y, p1.x, 0x05040100u);
-            v.w = __builtin_amdgcn_perm(p1.y, p1.x, 0x07060302u);
-        } else {
-            v = make_uint4(p0.x, p0.y, p1.x, p1.y);
-        }
-        if (st) u[i] = v;
-    }
+__device__ __forceinline__ void xp_fetch(const MmaArgs &A, XPos p, int cgmax, int cb0, int stride, uint32_t koff,
+                                         uint4 &v0, uint4 &v1) {
+    const int cg = min(p.cg, cgmax);
+    const uint32_t off = (uint32_t)p.t * (uint32_t)(2 * A.k) + (uint32_t)(cb0 + (cg >> 1) * stride) * 512u +
+                         xp_gbase<T>(cg & 1) + koff;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(A.x) + off);
+    const u32x4 a = src[0], b = src[1];
+    v0 = make_uint4(a.x, a.y, a.z, a.w);
+    v1 = make_uint4(b.x, b.y, b.z, b.w);
+}
+// The unit group of item (p, k): record (cb*4 + g)*n + t = (2*cg + (g & 1))*n + t.
+template <int T>
+__device__ __forceinline__ uint4 *xp_units(uint4 *xu, XPos p, int n, int k) {
+    return xu + ((2 * p.cg + xp_ge<T>(k)) * n + p.t) * kUnitsPerTok;
+}
+
+// Writes item k's pieces v0, v1 (pieces 2jp, 2jp+1) into its unit group u (if `st`:
+// the item exists):
+//   Q4_K, NVFP4, FP8: units 2jp, 2jp+1;
+//   Q5_K: piece j is the first (j < 4) or second half of units 2(j&3), 2(j&3)+1;
+//   Q6_K: piece j is half (j>>1)&1 of units s, s+2 with s = 4(j&1) + (j>>2);
+// each run of four Q4_K / Q5_K positions reordered [x0 x2][x1 x3].  Q4_K / Q5_K:
+// pieces 2jp, 2jp+1 are positions 16h .. 16h+15 of sub-block 2g + (jp >> 1), h = jp
+// & 1, and their hsum16 goes to float 2h + (jp >> 1) of the ninth unit.
+template <int T>
+__device__ __forceinline__ void xp_commit(int k, bool st, uint4 v0, uint4 v1, uint4 *u) {
+    const int jp = xp_jp<T>(k);
     if constexpr (T == T_Q4_K || T == T_Q5_K) {
-        // loads 0, 1: positions 16h..16h+15 of sub-block 2g; loads 2, 3: of 2g+1
-        const float p0 = hsum16(X.v[0], X.v[1]), p1 = hsum16(X.v[2], X.v[3]);
-        if (st) reinterpret_cast<float2 *>(xs + (q >> 1) * kUnitsPerTok + kXSumUnit)[q & 1] = make_float2(p0, p1);
+        // [x0 x1 x2 x3 x4 x5 x6 x7] -> [x0 x2] [x1 x3] [x4 x6] [x5 x7]
+        const uint4 w0 = make_uint4(__builtin_amdgcn_perm(v0.y, v0.x, 0x05040100u), __builtin_amdgcn_perm(v0.y, v0.x, 0x07060302u),
+                                    __builtin_amdgcn_perm(v0.w, v0.z, 0x05040100u), __builtin_amdgcn_perm(v0.w, v0.z, 0x07060302u));
+        const uint4 w1 = make_uint4(__builtin_amdgcn_perm(v1.y, v1.x, 0x05040100u), __builtin_amdgcn_perm(v1.y, v1.x, 0x07060302u),
+                                    __builtin_amdgcn_perm(v1.w, v1.z, 0x05040100u), __builtin_amdgcn_perm(v1.w, v1.z, 0x07060302u));
+        const float sum = hsum16(v0, v1);
+        if (st) {
+            if constexpr (T == T_Q4_K) {
+                u[2 * jp] = w0;
+                u[2 * jp + 1] = w1;
+            } else {
+                const int s0 = 4 * (jp & 1), half = jp >> 1;
+                reinterpret_cast<uint2 *>(u + s0)[half] = make_uint2(w0.x, w0.y);
+                reinterpret_cast<uint2 *>(u + s0 + 1)[half] = make_uint2(w0.z, w0.w);
+                reinterpret_cast<uint2 *>(u + s0 + 2)[half] = make_uint2(w1.x, w1.y);
+                reinterpret_cast<uint2 *>(u + s0 + 3)[half] = make_uint2(w1.z, w1.w);
+            }
+            reinterpret_cast<float *>(u + kXSumUnit)[2 * (jp & 1) + (jp >> 1)] = sum;
+        }
+    } else if constexpr (T == T_Q6_K) {
+        const int s0 = jp >> 1, half = jp & 1;
+        if (st) {
+            reinterpret_cast<uint2 *>(u + s0)[half] = make_uint2(v0.x, v0.y);
+            reinterpret_cast<uint2 *>(u + s0 + 2)[half] = make_uint2(v0.z, v0.w);
+            reinterpret_cast<uint2 *>(u + s0 + 4)[half] = make_uint2(v1.x, v1.y);
+            reinterpret_cast<uint2 *>(u + s0 + 6)[half] = make_uint2(v1.z, v1.w);
+        }
+    } else {
+        if (st) {
+            u[2 * jp] = v0;
+            u[2 * jp + 1] = v1;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Q4_K / Q5_K weight operand of step s.  Quant dword s of the lane's chunk holds
-// positions 4s..4s+3 of sub-block 2g (low nibbles) and of sub-block 2g+1 (high
-// nibbles).  Masked in place, each 16-bit half is an fp16 subnormal carrying the
-// quant in its mantissa: q * 2^-24 (low nibble, bits 0..3, Q5_K's fifth bit at 4) or
-// q * 2^-20 (high nibble, bits 4..7, fifth bit at 8); one packed fp16 fma per two
-// weights gives the exact operands o = (q - c)*sc*2^-14 of the split w = d*2^14*o +
-// r (kq_split).  Slot order of the step:
-//     (4s, 4s+2), (4s+1, 4s+3) of sub-block 2g, then the same of 2g+1.
+// Q4_K / Q5_K weight operands.  Quant dword l of the lane's chunk holds positions
+// 4l..4l+3 of sub-block 2g (low nibbles) and of sub-block 2g+1 (high nibbles).
+// Masked in place, each 16-bit half is an fp16 subnormal carrying the quant in its
+// mantissa: q * 2^-24 (low nibble, bits 0..3, Q5_K's fifth bit at 4) or q * 2^-20
+// (high nibble, bits 4..7, fifth bit at 8); one packed fp16 fma per two weights
+// gives the exact operands o = (q - c)*sc*2^-14 of the split w = d*2^14*o + r
+// (kq_split).  Q4_K: dwords 2e and 2e+1 give step e (positions 8e..8e+7 of
+// sub-block 2g, slots (8e, 8e+2), (8e+1, 8e+3), (8e+4, 8e+6), (8e+5, 8e+7)) from
+// their low nibbles and step 4 + e (the same positions of sub-block 2g+1) from their
+// high ones; the chain takes steps 0, 4, 1, 5, ... (each dword pair's two steps in
+// turn).  Q5_K: step s from dword s alone (q5_step).
 typedef KqSplit KqTile;
 
 template <bool Q5>
@@ -337,24 +420,34 @@ __device__ __forceinline__ KqTile kq_tile(const MRawKq &R, const KqLane &L) {
     return kq_split(R.hdr, L, Q5 ? 31.0f : 15.0f);
 }
 
-template <bool Q5>
-__device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int g, int s) {
+// Q4_K step e (HI = false: positions 8e..8e+7 of sub-block 2g) or 4 + e (HI: of 2g+1).
+template <bool HI>
+__device__ __forceinline__ h8 kq_step(const MRawKq &R, const KqTile &K, int e) {
+    const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+    const uint32_t m = HI ? 0x00F000F0u : 0x000F000Fu;
+    const uint32_t w0 = qw[2 * e], w1 = qw[2 * e + 1];
+    const uint32_t S = HI ? K.s1 : K.s0, C = HI ? K.c1 : K.c0;
+    return mk_h8(pkfma(w0 & m, S, C), pkfma((w0 >> 8) & m, S, C), pkfma(w1 & m, S, C), pkfma((w1 >> 8) & m, S, C));
+}
+
+// Q5_K step s from quant dword s alone: positions 4s..4s+3 of sub-block 2g, slots
+// (4s, 4s+2), (4s+1, 4s+3), then the same of 2g+1 (a Q5_K step built from two
+// dwords, as Q4_K's, needs registers the 16-wave kernels do not have).
+__device__ __forceinline__ h8 q5_step(const MRawKq &R, const KqTile &K, int g, int s) {
     const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
     const uint32_t w = qw[s], w8 = w >> 8;
     uint32_t lo02 = w & 0x000F000Fu, lo13 = w8 & 0x000F000Fu;
     uint32_t hi02 = w & 0x00F000F0u, hi13 = w8 & 0x00F000F0u;
-    if (Q5) {
-        // fifth bits: bit 2g (low sub-block) and 2g+1 (high) of qh byte l
-        const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
-        q5_fifth(hw[s] >> (2 * g), lo02, lo13, hi02, hi13);
-    }
+    // fifth bits: bit 2g (low sub-block) and 2g+1 (high) of qh byte l
+    const uint32_t hw[8] = {R.h0.x, R.h0.y, R.h0.z, R.h0.w, R.h1.x, R.h1.y, R.h1.z, R.h1.w};
+    q5_fifth(hw[s] >> (2 * g), lo02, lo13, hi02, hi13);
     return mk_h8(pkfma(lo02, K.s0, K.c0), pkfma(lo13, K.s0, K.c0), pkfma(hi02, K.s1, K.c1), pkfma(hi13, K.s1, K.c1));
 }
 
-// The same operands with the quant dword byte-paired first ([b0 b2 b1 b3]), so that
-// the slots of step s hold positions 4s..4s+3 of sub-block 2g and then 4s..4s+3 of
-// 2g+1 in order: the x of a step is two runs of four, which a stager can write
-// without permutes (the prefill's staging, p_xcommit).
+// The prefill's operands: step s from quant dword s alone, byte-paired first ([b0 b2
+// b1 b3]), so that its slots hold positions 4s..4s+3 of sub-block 2g and then
+// 4s..4s+3 of 2g+1 in order: the x of a step is two runs of four, which the
+// prefill's stager writes without permutes (p_xcommit).
 template <bool Q5>
 __device__ __forceinline__ h8 pkq_step(const MRawKq &R, const KqTile &K, int g, int s) {
     const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
@@ -474,11 +567,30 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
             f4 c1[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) c1[q] = (f4){0.f, 0.f, 0.f, 0.f};
+            if constexpr (PAIRED) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const h8 b = PAIRED ? pkq_step<T == T_Q5_K>(R[i], K, g, s) : kq_step<T == T_Q5_K>(R[i], K, g, s);
+                for (int s = 0; s < 8; ++s) {
+                    const h8 b = pkq_step<T == T_Q5_K>(R[i], K, g, s);
 #pragma unroll
-                for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
+                    for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
+                }
+            } else if constexpr (T == T_Q5_K) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const h8 b = q5_step(R[i], K, g, s);
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][s]), b, c1[q]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const h8 blo = kq_step<false>(R[i], K, e);
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][e]), blo, c1[q]);
+                    const h8 bhi = kq_step<true>(R[i], K, e);
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) c1[q] = mfma(u4h8(xv[q][4 + e]), bhi, c1[q]);
+                }
             }
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
@@ -543,35 +655,55 @@ __device__ __forceinline__ void msb(const typename MRawOf<T>::type (&R)[NT], int
 }
 
 // ---------------------------------------------------------------------------
-// Staging of x chunk [cb0, cb1) into LDS by the whole workgroup (8*n*cl
-// half-groups; blockDim is even, so the two halves of a group share a wave).
+// Staging of x chunk [cb0, cb1) into LDS by the whole workgroup (16*n*cl items,
+// IP per thread and pass: two, or one where the accumulators leave no registers).
 // `issue` runs between the last pass's x loads and their LDS writes, so loads it
 // issues (the first weight superblocks) are in flight while that x arrives; the
 // in-order load counter lets the writes wait for x alone.
-template <int T, class F>
+template <int T, int IP, class F>
 __device__ __forceinline__ void x_stage_then(const MmaArgs &A, uint4 *xu, int cb0, int cb1, F &&issue) {
-    const int halves = 8 * A.n * (cb1 - cb0);   // > 0
-    const int bd = (int)blockDim.x;
-    const int w64 = 64 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    static_assert(IP == 1 || IP == 2, "one or two items per pass");
+    const int n = A.n;
+    const int items = 16 * n * (cb1 - cb0);   // > 0
+    const int bd = (int)blockDim.x;           // a multiple of 64
+    const int tid = (int)threadIdx.x, k = tid & 7;
+    const int w64 = 64 * __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cgmax = 2 * (cb1 - cb0) - 1;
+    const XPos dstep = xpos_of(A, bd >> 3);   // bd / 8 record pairs per pass step (uniform)
     int q0 = 0;
-    for (; q0 + bd < halves; q0 += bd) {   // full passes (uniform trip count)
-        const int q = q0 + (int)threadIdx.x;
-        XHalf X;
-        xhalf_fetch<T>(A, q, cb0, 1, X);
-        xhalf_commit<T>(q, true, X, xu);
+    for (; q0 + IP * bd < items; q0 += IP * bd) {   // full passes (uniform trip count)
+        uint4 v[2 * IP];
+        const XPos p = xpos_of(A, (q0 + tid) >> 3);
+        uint4 *const u0 = xp_units<T>(xu, p, n, k);
+        if constexpr (IP == 2) {
+            const XPos p1 = xpos_step(p, n, dstep.t, dstep.cg);
+            uint4 *const u1 = xp_units<T>(xu, p1, n, k);
+            xp_fetch<T>(A, p, cgmax, cb0, 1, xp_koff<T>(k), v[0], v[1]);
+            xp_fetch<T>(A, p1, cgmax, cb0, 1, xp_koff<T>(k), v[IP], v[IP + 1]);
+            xp_commit<T>(k, true, v[0], v[1], u0);
+            xp_commit<T>(k, true, v[IP], v[IP + 1], u1);
+        } else {
+            xp_fetch<T>(A, p, cgmax, cb0, 1, xp_koff<T>(k), v[0], v[1]);
+            xp_commit<T>(k, true, v[0], v[1], u0);
+        }
     }
-    const bool has = q0 + w64 < halves;   // scalar: the wave has half-groups in the last pass
-    const int q = q0 + (int)threadIdx.x;
-    XHalf X;
-    if (has) xhalf_fetch<T>(A, q < halves ? q : halves - 1, cb0, 1, X);
+    // The last pass: each item's loads go out where the wave has items there (a scalar test).
+    uint4 v[4];
+    const XPos p = xpos_of(A, (q0 + tid) >> 3);
+    const XPos p1 = xpos_step(p, n, dstep.t, dstep.cg);
+    uint4 *const u0 = xp_units<T>(xu, p, n, k), *const u1 = xp_units<T>(xu, p1, n, k);
+    const bool h0 = q0 + w64 < items, h1 = IP == 2 && q0 + bd + w64 < items;
+    if (h0) xp_fetch<T>(A, p, cgmax, cb0, 1, xp_koff<T>(k), v[0], v[1]);
+    if (h1) xp_fetch<T>(A, p1, cgmax, cb0, 1, xp_koff<T>(k), v[2], v[3]);
     __builtin_amdgcn_sched_barrier(0);
     issue();
     __builtin_amdgcn_sched_barrier(0);
-    if (has) xhalf_commit<T>(q, q < halves, X, xu);
+    if (h0) xp_commit<T>(k, q0 + tid < items, v[0], v[1], u0);
+    if (h1) xp_commit<T>(k, q0 + bd + tid < items, v[2], v[3], u1);
 }
-template <int T>
+template <int T, int IP>
 __device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, int cb1) {
-    x_stage_then<T>(A, xu, cb0, cb1, [] {});
+    x_stage_then<T, IP>(A, xu, cb0, cb1, [] {});
 }
 
 // The body for one weight type.  The wave serves NT row tiles (`wr[i]`/`sr[i]` = its
@@ -582,7 +714,7 @@ __device__ __forceinline__ void x_stage(const MmaArgs &A, uint4 *xu, int cb0, in
 // are wave-uniform scalars).
 //
 // Decode path: when every wave's superblocks fit one round of loads and their x
-// fits one staging half-group per lane, each wave stages its own x (see below).  Otherwise a ring of kDepth superblocks
+// fits four staging rounds of two x items per lane, each wave stages its own x (see below).  Otherwise a ring of kDepth superblocks
 // refills behind the computation, and x is staged in chunks of A.kc superblocks in
 // turn; every wave steps through every chunk (two barriers per step), whether or
 // not it has superblocks there, so all waves meet the same barriers.
@@ -595,6 +727,8 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
     // Ring depth D; unroll U, a multiple of D and of NP, so that ring slots and
     // accumulator sets are compile-time indices.
     constexpr int U = D > NP ? D : NP;
+    // x items per thread and staging pass (four phases of two token groups: one).
+    constexpr int IP = NP * NG >= 8 ? 1 : 2;
     static_assert(U % D == 0 && U % NP == 0, "ring and phase sets must tile the unroll");
     const int n = A.n, nb = A.nb, kc = A.kc;
     const uint4 *zero = lds;   // kZeroUnits units of zeros
@@ -611,7 +745,10 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
     // which meets no barrier after the zeros are written, the wave's own units:
     // their rows of the product are never stored.
     const KqLane L = kq_lane_consts(g);   // K-quant scale-table selectors of the lane group
-    int lane_units[NG];   // the lane's (g, token) unit group, superblock 0
+    // The lane's (g, token) unit group of superblock 0, hoisted out of the loop with
+    // two token groups (with one, the kernels that must fit 96 registers compute it
+    // in place).
+    int lane_units[NG];
 #pragma unroll
     for (int q = 0; q < NG; ++q) lane_units[q] = (g * n + 16 * q + t) * kUnitsPerTok;
     auto xa_of = [&](int cb, const uint4 *(&xa)[NG], const uint4 *other) {
@@ -619,11 +756,12 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
             const int tok = 16 * q + t;
-            xa[q] = tok < n ? xu + (lane_units[q] + cbo) : other;
+            const int lu = NG == 1 ? (g * n + t) * kUnitsPerTok : lane_units[q];
+            xa[q] = tok < n ? xu + (lu + cbo) : other;
         }
     };
 
-    if (NP == 1 && dec) {   // (NP > 1: never) the host guarantees maxcnt <= D and 8 * n * maxcnt <= 64 * kMmaDecRounds
+    if (NP == 1 && dec) {   // (NP > 1: never) the host guarantees maxcnt <= D and 16 * n * maxcnt <= 128 * kMmaDecRounds
         // Each wave stages the x of its own superblocks in a region of its own: its x
         // loads go out ahead of its weight loads, the in-order load counter lets it
         // wait for x alone, and no barrier ties it to the other waves (whose loads,
@@ -635,21 +773,35 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int lane = tid & 63;
         xu += wave * (maxcnt * 4 * n * kUnitsPerTok);
-        const int hq = 8 * n * cnt;   // this wave's half-groups (wave-uniform), one per lane and round
+        const int hq = 16 * n * cnt;   // this wave's x items (wave-uniform), two per lane and round
+        const int cgmax = 2 * cnt - 1;
+        const XPos dstep = xpos_of(A, 8);   // eight record pairs per round step
+        const int k = lane & 7;
         Raw ring[D][NT];
         int q0 = 0;
-        for (; q0 + 64 < hq; q0 += 64) {   // full rounds (several tokens)
-            XHalf X;
-            xhalf_fetch<T>(A, q0 + lane, kw, KW, X);
-            xhalf_commit<T>(q0 + lane, true, X, xu);
+        for (; q0 + 128 < hq; q0 += 128) {   // full rounds (several tokens)
+            uint4 v[4];
+            const XPos p = xpos_of(A, (q0 + lane) >> 3);
+            const XPos p1 = xpos_step(p, n, dstep.t, dstep.cg);
+            uint4 *const u0 = xp_units<T>(xu, p, n, k), *const u1 = xp_units<T>(xu, p1, n, k);
+            xp_fetch<T>(A, p, cgmax, kw, KW, xp_koff<T>(k), v[0], v[1]);
+            xp_fetch<T>(A, p1, cgmax, kw, KW, xp_koff<T>(k), v[2], v[3]);
+            xp_commit<T>(k, true, v[0], v[1], u0);
+            xp_commit<T>(k, true, v[2], v[3], u1);
         }
         {   // the last round, its loads ahead of the first weight loads
-            XHalf X;
-            const int q = q0 + lane;
-            if (cnt > 0) xhalf_fetch<T>(A, q < hq ? q : hq - 1, kw, KW, X);
+            uint4 v[4];
+            const XPos p = xpos_of(A, (q0 + lane) >> 3);
+            const XPos p1 = xpos_step(p, n, dstep.t, dstep.cg);
+            uint4 *const u0 = xp_units<T>(xu, p, n, k), *const u1 = xp_units<T>(xu, p1, n, k);
+            const bool h0 = q0 < hq, h1 = q0 + 64 < hq;
+            if (h0) xp_fetch<T>(A, p, cgmax, kw, KW, xp_koff<T>(k), v[0], v[1]);
+            if (h1) xp_fetch<T>(A, p1, cgmax, kw, KW, xp_koff<T>(k), v[2], v[3]);
 #pragma unroll
             for (int i = 0; i < NT; ++i) ring[0][i] = mload<T>(wr[i], wo[i], sr[i], min(kw, lastb), g, sbs, tl);
-            if (cnt > 0) xhalf_commit<T>(q, q < hq, X, xu);   // LDS order within a wave: no barrier
+            // LDS order within a wave: no barrier
+            if (h0) xp_commit<T>(k, q0 + lane < hq, v[0], v[1], u0);
+            if (h1) xp_commit<T>(k, q0 + 64 + lane < hq, v[2], v[3], u1);
         }
 #pragma unroll
         for (int u = 0; u < D; ++u) {
@@ -673,7 +825,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
     }
 
     Raw ring[D][NT];
-    x_stage_then<T>(A, xu, 0, min(nb, kc), [&] {   // the ring's loads go out behind the first x loads
+    x_stage_then<T, IP>(A, xu, 0, min(nb, kc), [&] {   // the ring's loads go out behind the first x loads
 #pragma unroll
         for (int u = 0; u < D; ++u)
 #pragma unroll
@@ -690,7 +842,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
                 while (b >= (chunk + 1) * kc) {   // scalar
                     ++chunk;
                     __syncthreads();
-                    x_stage<T>(A, xu, chunk * kc, min(nb, (chunk + 1) * kc));
+                    x_stage<T, IP>(A, xu, chunk * kc, min(nb, (chunk + 1) * kc));
                     __syncthreads();
                 }
                 const uint4 *xa[NG];
@@ -707,7 +859,7 @@ __device__ __forceinline__ void mma_body(const MmaArgs &A, int KW, int kw, int s
     while (chunk + 1 < nchunks) {
         ++chunk;
         __syncthreads();
-        x_stage<T>(A, xu, chunk * kc, min(nb, (chunk + 1) * kc));
+        x_stage<T, IP>(A, xu, chunk * kc, min(nb, (chunk + 1) * kc));
         __syncthreads();
     }
 }
@@ -741,17 +893,17 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     // Ring depth: three superblocks with one phase per wave; with several, four (two
     // in 16-wave workgroups, which have 128 registers, and one there with four phases
     // of two token groups, whose accumulators alone take 32 of them).
-    // 16-wave instances for two token groups that can hold Q6_K keep two (their
-    // decode path never has more than one superblock per wave: 8 * n * count <= 256
-    // with n > 16).
-    constexpr int D = NP == 1 ? (((TS & TS_Q6) && NG == 2 && WV == 16) ? 2 : kDepth)
+    // 16-wave instances for two token groups that can hold Q5_K or Q6_K keep two
+    // (their decode path never has more than one superblock per wave: 16 * n * count
+    // <= 512 with n > 16).
+    constexpr int D = NP == 1 ? (((TS & (TS_Q5 | TS_Q6)) && NG == 2 && WV == 16) ? 2 : kDepth)
                               : (WV <= 8 ? 4 : (NP == 4 && NG == 2 ? 1 : 2));
     const int j = lane & 15, g = lane >> 4;
     const int up = SW ? (rt & 1) : 0;   // SwiGLU: 0 for a gate tile group, 1 for an up one
     const int64_t unit = SW ? (int64_t)(bid - S.wg_begin) * (tpw >> 1) + (rt >> 1)
                             : (int64_t)(bid - S.wg_begin) * tpw + rt;
-    int64_t rows[NT];
-    rows[0] = unit * 16 + j;
+    int rows[NT];   // < m + 16 <= 2^31
+    rows[0] = (int)(unit * 16 + j);
     const int n = A.n;
     if (threadIdx.x < kZeroUnits) lds[threadIdx.x] = make_uint4(0, 0, 0, 0);
 
@@ -801,6 +953,8 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     // phase) and the tile's first wave adds the KS slots in order.
     constexpr int per = NT * NG;   // 16-byte partials per lane
     f4 *part = reinterpret_cast<f4 *>(lds);
+    // The lane index again, from the exec mask (nothing to keep alive through the body).
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     f4(&acc)[NT][NG] = ph[0];
     if (KW == 1) {
 #pragma unroll
@@ -820,7 +974,7 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
 #pragma unroll
                 for (int i = 0; i < NT; ++i)
 #pragma unroll
-                    for (int q = 0; q < NG; ++q) part[(slot * per + i * NG + q) * 64 + lane] = ph[a][i][q];
+                    for (int q = 0; q < NG; ++q) part[(slot * per + i * NG + q) * 64 + ln] = ph[a][i][q];
             }
         }
         __syncthreads();
@@ -831,7 +985,7 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
             for (int i = 0; i < NT; ++i)
 #pragma unroll
                 for (int q = 0; q < NG; ++q) {
-                    const f4 v = part[(slot * per + i * NG + q) * 64 + lane];
+                    const f4 v = part[(slot * per + i * NG + q) * 64 + ln];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[i][q][e] += v[e];
                 }
@@ -840,7 +994,7 @@ __global__ __launch_bounds__(64 * WV, (mma_min_waves<TS, NG, NT, NP>())) void mm
     if (SW) {
         // The waves left hold their tile group's sums (one per group).  LDS from A.xch
         // on is used by nothing else, so the gate sums go there at once.
-        f4 *xch = reinterpret_cast<f4 *>(lds + A.xch) + (rt >> 1) * NG * 64 + lane;
+        f4 *xch = reinterpret_cast<f4 *>(lds + A.xch) + (rt >> 1) * NG * 64 + ln;
         if (!up) {
 #pragma unroll
             for (int q = 0; q < NG; ++q) xch[q * 64] = acc[0][q];

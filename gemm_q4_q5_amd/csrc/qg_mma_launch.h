@@ -9,7 +9,7 @@ namespace qg {
 // Weight superblocks each wave keeps in flight (a ring refills behind the
 // computation when a wave has more).
 constexpr int kMmaDepth = 3;
-// Decode path: staging rounds of one x half-group (64 halves) per lane, at most.
+// Decode path: staging rounds of two 32-byte x items per lane, at most.
 constexpr int kMmaDecRounds = 4;
 
 struct MSeg {
@@ -29,7 +29,7 @@ struct MSeg {
     int32_t wg_begin;        // first workgroup of this matrix
     int32_t dec;             // 1: every wave stages its own x (decode path, np = 1; needs
                              //    ceil(nb/ks) <= kMmaDepth (2 with two tiles per wave),
-                             //    8*n*ceil(nb/ks) <= 64*kMmaDecRounds, and LDS for
+                             //    16*n*ceil(nb/ks) <= 128*kMmaDecRounds, and LDS for
                              //    wv*ceil(nb/ks)*n*576 bytes after the 144 of zeros)
     int32_t tiled;           // K-quants: 16-row tiled layout (qg_weight.layout = QG_LAYOUT_TILES)
 };

@@ -51,7 +51,7 @@ __device__ __forceinline__ void p_xcommit(int q, const XHalf &X, uint4 *xs) {
         const uint2 p0 = xhalf_piece<T>(X, i, 0), p1 = xhalf_piece<T>(X, i, 1);
         u[i] = make_uint4(p0.x, p0.y, p1.x, p1.y);
     }
-    if constexpr (T == T_Q4_K || T == T_Q5_K) {   // the sub-block sums, as in xhalf_commit
+    if constexpr (T == T_Q4_K || T == T_Q5_K) {   // the sub-block sums, half by half as in the product
         const float s0 = hsum16(X.v[0], X.v[1]), s1 = hsum16(X.v[2], X.v[3]);
         reinterpret_cast<float2 *>(xs + (q >> 1) * kUnitsPerTok + kXSumUnit)[q & 1] = make_float2(s0, s1);
     }
