@@ -286,3 +286,29 @@ def test_maximum_k(wt):
     yp = qg.qgemm_prefill(w, xd[:3])
     torch.cuda.synchronize()
     assert_within(yp.cpu().numpy(), y_ref[:3], a[:3], what=f"max k prefill type {wt}")
+
+
+# Q6_K with 16 phases and more than 8192 rows at 17..32 tokens: the host's grid search
+# would pick 16-wave workgroups of four phases, an instance that is not built (it does
+# not fit 128 registers); the fallback (8-wave workgroups, four phases) must keep every
+# row's one-token bits and the oracle's tolerance.
+def test_q6k_many_rows_two_token_groups():
+    import torch
+    m, k = 12288, 9728
+    print(f"q6k {m}x{k} n=17,32", flush=True)
+    w, data, scales = weight(qg.Q6_K, m, k, 331)
+    x = synth.duplicate_rows(synth.activations(32, k, synth.rng_for(332)))
+    xd = x_dev(x)
+    toks = (0, 5, 16, 31)
+    singles = {t: bits(qg.qgemv(w, xd[t])) for t in toks}
+    for n in (17, 32):
+        y = qg.qgemm_rows(w, xd[:n])
+        torch.cuda.synchronize()
+        yb = bits(y)
+        for t in toks:
+            if t < n:
+                assert np.array_equal(yb[t], singles[t]), f"n={n} row {t} differs from n=1"
+    rng = synth.rng_for(333)
+    rows = np.unique(np.concatenate([[0, 8191, 8192, m - 1], rng.choice(m, size=64, replace=False)]))
+    y_ref, a = oracle.gemm(qg.Q6_K, data, scales, m, k, x, rows=rows)
+    assert_within(y.cpu().numpy()[:, rows], y_ref, a, what="q6k many rows")
