@@ -63,7 +63,8 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
     constexpr int HPT = 8 * BM / NTH;   // x half-groups per thread and superblock
     static_assert(HPT >= 1 && (8 * BM) % NTH == 0, "token block too small");
     typedef typename MRawOf<T>::type Raw;
-    extern __shared__ uint4 lds[];   // the block's x for one superblock: 4 * BM * 9 units
+    extern __shared__ uint4 lds[];   // two buffers of the block's x for one superblock, 4 * BM * 9 units each
+    constexpr int XU = 4 * BM * kUnitsPerTok;
 
     const int tid = (int)threadIdx.x, lane = tid & 63;
     const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);   // row group
@@ -99,12 +100,12 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
 #pragma unroll
         for (int q = 0; q < NG; ++q) acc[i][q] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    // One superblock: the MFMAs of ring slot R over the staged x.
+    // One superblock: the MFMAs of ring slot R over the x staged in buffer `buf`.
     const uint4 *xl = lds + (g * BM + j) * kUnitsPerTok;   // the lane's token, step 0
-    auto compute = [&](Raw (&R)[NT]) __attribute__((always_inline)) {
+    auto compute = [&](Raw (&R)[NT], int buf) __attribute__((always_inline)) {
         const uint4 *xa[NG];
 #pragma unroll
-        for (int q = 0; q < NG; ++q) xa[q] = xl + 16 * q * kUnitsPerTok;
+        for (int q = 0; q < NG; ++q) xa[q] = xl + buf * XU + 16 * q * kUnitsPerTok;
         msb<T, NT, NG, true>(R, g, L, xa, acc);
         // The compiler's interleaving of the MFMAs with the operand construction and
         // the x reads (mode 1): 3-4 % faster at 512 tokens than its default order.
@@ -126,42 +127,41 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
             }
         }
     };
-    auto commit_x = [&](const XHalf (&X)[HPT]) __attribute__((always_inline)) {
+    auto commit_x = [&](const XHalf (&X)[HPT], int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < HPT; ++v) p_xcommit<T>(tid + NTH * v, X[v], lds);
+        for (int v = 0; v < HPT; ++v) p_xcommit<T>(tid + NTH * v, X[v], lds + buf * XU);
     };
 
-    // Per superblock b: b+1's weights and x go out, b is computed, barrier, b+1's x
-    // is written to LDS, barrier.
+    // Per superblock b: b+1's weights and x go out, b is computed from x buffer b % 2,
+    // b+1's x is written to the other buffer, one barrier.  That buffer was last read
+    // by the computation of b-1, which every wave finished before the previous barrier.
     Raw ring0[NT], ring1[NT];
     XHalf X[HPT];
     load_w(ring0, 0);
     fetch_x(X, 0);
-    commit_x(X);
+    commit_x(X, 0);
     __syncthreads();
-    // Two superblocks per trip so that the ring slots are compile-time.  The loads are
-    // unconditional (the superblock index clamped to the last one; a redundant load at
-    // the end): loads under a branch make the compiler wait for them at the join.  The
-    // scheduling barriers keep them ahead of the computation (left alone, the compiler
-    // sinks them to its end, which exposes their whole latency).
+    // Two superblocks per trip so that the ring slots and buffers are compile-time.  The
+    // loads are unconditional (the superblock index clamped to the last one; a redundant
+    // load at the end): loads under a branch make the compiler wait for them at the join.
+    // The scheduling barriers keep them ahead of the computation (left alone, the
+    // compiler sinks them to its end, which exposes their whole latency).
     for (int b = 0; b < nb; b += 2) {
         __builtin_amdgcn_sched_barrier(0);
         load_w(ring1, min(b + 1, nb - 1));
         fetch_x(X, min(b + 1, nb - 1));
         __builtin_amdgcn_sched_barrier(0);
-        compute(ring0);
-        __syncthreads();
+        compute(ring0, 0);
         if (b + 1 >= nb) break;   // uniform
-        commit_x(X);
+        commit_x(X, 1);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         load_w(ring0, min(b + 2, nb - 1));
         fetch_x(X, min(b + 2, nb - 1));
         __builtin_amdgcn_sched_barrier(0);
-        compute(ring1);
-        __syncthreads();
+        compute(ring1, 1);
         if (b + 2 >= nb) break;
-        commit_x(X);
+        commit_x(X, 0);
         __syncthreads();
     }
 
@@ -184,7 +184,7 @@ static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
     constexpr int BM = 16 * NG, BN = 16 * WV * NT;
     const int64_t blocks = (A.m + BN - 1) / BN * ((A.n + BM - 1) / BM);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)4 * BM * kUnitsPerTok * 16;
+    const size_t lds = (size_t)2 * 4 * BM * kUnitsPerTok * 16;   // two x buffers
     const void *fn = (const void *)prefill_kernel<T, NT, NG, WV>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
