@@ -217,7 +217,7 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_m
 //   NVFP4:     64g + 8s + 0..7
 //   FP8:       128(s >> 2) + 32g + 8(s & 3) + 0..7   (steps 0..3 and 4..7 each stay
 //              inside one 128-wide scale block)
-// (The prefill GEMM stages its own x, in the orders of pkq_step and q6_dword.)
+// (The prefill GEMM stages x with the same items, in the orders of pkq_step and q6_dword.)
 constexpr int kUnitsPerTok = 9;
 constexpr int kZeroUnits = 9;
 // Q4_K / Q5_K: the ninth unit of (cb, g, t) holds the fp32 sums of x over the lane
@@ -243,50 +243,10 @@ __device__ __forceinline__ void slot_pieces(int g, int s, int &o0, int &o1) {
     }
 }
 
-// The prefill's staging half-group: the x behind units 4h .. 4h+3 of one
-// (superblock, lane group, token), fetched as four 16-byte loads from one base.
-struct XHalf {
-    uint4 v[4];
-};
-
-// Offset (in halves, from the superblock) of a half-group's base, and where the
-// two 8-byte pieces of its step 4h + i sit among the four loads.
-template <int T>
-__device__ __forceinline__ int xhalf_base(int g, int h) {
-    if constexpr (T == T_Q6_K) return 128 * (g >> 1) + 16 * (g & 1) + 8 * h;
-    else if constexpr (T == T_NVFP4) return 64 * g + 32 * h;
-    else if constexpr (T == T_FP8) return 128 * h + 32 * g;
-    else return 64 * g + 16 * h;
-}
-// Loads at base + {0, 8, 32, 40} (Q4_K/Q5_K), {0, 64, 32, 96} (Q6_K), {0, 8, 16, 24} (NVFP4).
-template <int T>
-__device__ __forceinline__ int xhalf_off(int l) {
-    if constexpr (T == T_Q6_K) return (l & 1) * 64 + (l >> 1) * 32;
-    else if constexpr (T == T_NVFP4 || T == T_FP8) return 8 * l;
-    else return (l & 1) * 8 + (l >> 1) * 32;
-}
-template <int T>
-__device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
-    uint4 v;
-    int hi;
-    if constexpr (T == T_Q6_K) {
-        v = X.v[2 * e + (i & 1)];
-        hi = i >> 1;
-    } else if constexpr (T == T_NVFP4 || T == T_FP8) {
-        v = X.v[i];
-        hi = e;
-    } else {
-        v = X.v[2 * e + (i >> 1)];
-        hi = i & 1;
-    }
-    return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
-}
-
 // Staging by items of 32 bytes.  Lane groups 2gh and 2gh+1 of (staged superblock
 // cb, token t) take 256 bytes of x (one run; FP8: two 128-byte lines), eight items
 // of two 16-byte pieces each; item i has r2 = i >> 3 = (cb*2 + gh)*n + t and k =
-// i & 7, which names its lane group 2gh + xp_ge(k) and its pieces 2jp, 2jp+1 (jp =
-// xp_jp(k)) of that group's eight, piece j the x behind unit j (see xp_commit).
+// i & 7, which names its lane group 2gh + xp_ge(k) and its units (see xp_commit).
 // Consecutive lanes take consecutive items, so each quad of lanes in a load reads
 // one whole 128-byte line.  (Lanes that fetched the four loads of half a unit group
 // touched two lines per quad: the 32-token calls staged x 15-20 % slower, the
@@ -299,7 +259,14 @@ __device__ __forceinline__ uint2 xhalf_piece(const XHalf &X, int i, int e) {
 template <int T>
 __device__ __forceinline__ uint32_t xp_koff(int k) {
     if constexpr (T == T_FP8) return 256u * (uint32_t)(k >> 2) + 32u * (uint32_t)(k & 3);
+    else if constexpr (T == T_Q6_K) return 128u * (uint32_t)(k >> 2) + 16u * (uint32_t)(k & 3);
     else return 32u * (uint32_t)k;
+}
+// Bytes from an item's first 16-byte piece to its second: adjacent, or for Q6_K the
+// 32 positions further on that complete the same two units.
+template <int T>
+__device__ __forceinline__ constexpr int xp_second() {
+    return T == T_Q6_K ? 64 : 16;
 }
 template <int T>
 __device__ __forceinline__ uint32_t xp_gbase(int gh) {
@@ -307,13 +274,13 @@ __device__ __forceinline__ uint32_t xp_gbase(int gh) {
 }
 template <int T>
 __device__ __forceinline__ int xp_ge(int k) {
-    if constexpr (T == T_Q6_K) return k & 1;
+    if constexpr (T == T_Q6_K) return (k >> 1) & 1;
     else if constexpr (T == T_FP8) return (k >> 1) & 1;
     else return k >> 2;
 }
 template <int T>
 __device__ __forceinline__ int xp_jp(int k) {
-    if constexpr (T == T_Q6_K) return k >> 1;
+    if constexpr (T == T_Q6_K) return 4 * (k & 1) + (k >> 2);   // its first unit (the second: + 2)
     else if constexpr (T == T_FP8) return 2 * (k >> 2) + (k & 1);
     else return k & 3;
 }
@@ -343,8 +310,8 @@ __device__ __forceinline__ void xp_fetch(const MmaArgs &A, XPos p, int cgmax, in
     const int cg = min(p.cg, cgmax);
     const uint32_t off = (uint32_t)p.t * (uint32_t)(2 * A.k) + (uint32_t)(cb0 + (cg >> 1) * stride) * 512u +
                          xp_gbase<T>(cg & 1) + koff;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(A.x) + off);
-    const u32x4 a = src[0], b = src[1];
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(A.x) + off;
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(src), b = *reinterpret_cast<const u32x4 *>(src + xp_second<T>());
     v0 = make_uint4(a.x, a.y, a.z, a.w);
     v1 = make_uint4(b.x, b.y, b.z, b.w);
 }
@@ -358,14 +325,27 @@ __device__ __forceinline__ uint4 *xp_units(uint4 *xu, XPos p, int n, int k) {
 // the item exists):
 //   Q4_K, NVFP4, FP8: units 2jp, 2jp+1;
 //   Q5_K: piece j is the first (j < 4) or second half of units 2(j&3), 2(j&3)+1;
-//   Q6_K: piece j is half (j>>1)&1 of units s, s+2 with s = 4(j&1) + (j>>2);
-// each run of four Q4_K / Q5_K positions reordered [x0 x2][x1 x3].  Q4_K / Q5_K:
-// pieces 2jp, 2jp+1 are positions 16h .. 16h+15 of sub-block 2g + (jp >> 1), h = jp
-// & 1, and their hsum16 goes to float 2h + (jp >> 1) of the ninth unit.
-template <int T>
+//   Q6_K: the item's two pieces (positions P .. P+7 and P+32 .. P+39 of its lane
+//     group, bytes xp_koff and xp_koff + 64 of the record pair) are the first and
+//     second runs of units jp and jp + 2 (jp = 4(k&1) + (k>>2));
+// each run of four Q4_K / Q5_K positions reordered [x0 x2][x1 x3].  NATURAL (the
+// prefill's order of pkq_step): Q4_K and Q5_K both as Q5_K, runs in natural order.
+// Q4_K / Q5_K: pieces 2jp, 2jp+1 are positions 16h .. 16h+15 of sub-block 2g + (jp >>
+// 1), h = jp & 1, and their hsum16 goes to float 2h + (jp >> 1) of the ninth unit.
+template <int T, bool NATURAL = false>
 __device__ __forceinline__ void xp_commit(int k, bool st, uint4 v0, uint4 v1, uint4 *u) {
     const int jp = xp_jp<T>(k);
-    if constexpr (T == T_Q4_K || T == T_Q5_K) {
+    if constexpr ((T == T_Q4_K || T == T_Q5_K) && NATURAL) {
+        const float sum = hsum16(v0, v1);
+        if (st) {
+            const int s0 = 4 * (jp & 1), half = jp >> 1;
+            reinterpret_cast<uint2 *>(u + s0)[half] = make_uint2(v0.x, v0.y);
+            reinterpret_cast<uint2 *>(u + s0 + 1)[half] = make_uint2(v0.z, v0.w);
+            reinterpret_cast<uint2 *>(u + s0 + 2)[half] = make_uint2(v1.x, v1.y);
+            reinterpret_cast<uint2 *>(u + s0 + 3)[half] = make_uint2(v1.z, v1.w);
+            reinterpret_cast<float *>(u + kXSumUnit)[2 * (jp & 1) + (jp >> 1)] = sum;
+        }
+    } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
         // [x0 x1 x2 x3 x4 x5 x6 x7] -> [x0 x2] [x1 x3] [x4 x6] [x5 x7]
         const uint4 w0 = make_uint4(__builtin_amdgcn_perm(v0.y, v0.x, 0x05040100u), __builtin_amdgcn_perm(v0.y, v0.x, 0x07060302u),
                                     __builtin_amdgcn_perm(v0.w, v0.z, 0x05040100u), __builtin_amdgcn_perm(v0.w, v0.z, 0x07060302u));
@@ -386,12 +366,10 @@ __device__ __forceinline__ void xp_commit(int k, bool st, uint4 v0, uint4 v1, ui
             reinterpret_cast<float *>(u + kXSumUnit)[2 * (jp & 1) + (jp >> 1)] = sum;
         }
     } else if constexpr (T == T_Q6_K) {
-        const int s0 = jp >> 1, half = jp & 1;
+        // v0 = positions P .. P+7, v1 = P+32 .. P+39: the two runs of units jp and jp + 2
         if (st) {
-            reinterpret_cast<uint2 *>(u + s0)[half] = make_uint2(v0.x, v0.y);
-            reinterpret_cast<uint2 *>(u + s0 + 2)[half] = make_uint2(v0.z, v0.w);
-            reinterpret_cast<uint2 *>(u + s0 + 4)[half] = make_uint2(v1.x, v1.y);
-            reinterpret_cast<uint2 *>(u + s0 + 6)[half] = make_uint2(v1.z, v1.w);
+            u[jp] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+            u[jp + 2] = make_uint4(v0.z, v0.w, v1.z, v1.w);
         }
     } else {
         if (st) {
@@ -447,7 +425,7 @@ __device__ __forceinline__ h8 q5_step(const MRawKq &R, const KqTile &K, int g, i
 // The prefill's operands: step s from quant dword s alone, byte-paired first ([b0 b2
 // b1 b3]), so that its slots hold positions 4s..4s+3 of sub-block 2g and then
 // 4s..4s+3 of 2g+1 in order: the x of a step is two runs of four, which the
-// prefill's stager writes without permutes (p_xcommit).
+// prefill's stager writes without permutes (xp_commit, NATURAL).
 template <bool Q5>
 __device__ __forceinline__ h8 pkq_step(const MRawKq &R, const KqTile &K, int g, int s) {
     const uint32_t qw[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};

@@ -31,37 +31,17 @@
 
 namespace qg {
 
-// x staging.  Half-group q = ((g * BM + t) << 1) | h of the block's x for a
-// superblock: token t0 + t (clamped to the last), the x behind units 4h .. 4h+3 of
-// lane group g, i.e. four 16-byte loads from p_xsrc(q) + 256 * b halves at the
-// offsets xhalf_off, written as units (g * BM + t) * 9 + 4h + i, each unit the two
-// 8-byte pieces of step 4h + i in order (the operand order of pkq_step, q6_steps,
-// f4_step and f8_step: no permutes), and the Q4_K / Q5_K sub-block sums in unit 8.
-template <int T, int BM>
-__device__ __forceinline__ const _Float16 *p_xsrc(const PrefillArgs &A, int64_t t0, int q) {
-    const int h = q & 1, r = q >> 1, t = r % BM, g = r / BM;
-    const int64_t tok = t0 + t < A.n ? t0 + t : A.n - 1;
-    return reinterpret_cast<const _Float16 *>(A.x) + tok * A.k + xhalf_base<T>(g, h);
-}
-template <int T>
-__device__ __forceinline__ void p_xcommit(int q, const XHalf &X, uint4 *xs) {
-    uint4 *u = xs + (q >> 1) * kUnitsPerTok + 4 * (q & 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint2 p0 = xhalf_piece<T>(X, i, 0), p1 = xhalf_piece<T>(X, i, 1);
-        u[i] = make_uint4(p0.x, p0.y, p1.x, p1.y);
-    }
-    if constexpr (T == T_Q4_K || T == T_Q5_K) {   // the sub-block sums, half by half as in the product
-        const float s0 = hsum16(X.v[0], X.v[1]), s1 = hsum16(X.v[2], X.v[3]);
-        reinterpret_cast<float2 *>(xs + (q >> 1) * kUnitsPerTok + kXSumUnit)[q & 1] = make_float2(s0, s1);
-    }
-}
-
 template <int T, int NT, int NG, int WV>
 __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A) {
     constexpr int BM = 16 * NG, BN = 16 * WV * NT, NTH = 64 * WV;
-    constexpr int HPT = 8 * BM / NTH;   // x half-groups per thread and superblock
-    static_assert(HPT >= 1 && (8 * BM) % NTH == 0, "token block too small");
+    // x staging by 32-byte items (xp_koff, xp_gbase, xp_commit): for a superblock the
+    // block's x is 16*BM items; thread tid takes items tid + NTH*v, v < IPT, item i
+    // having record pair r2 = i >> 3 (lane groups 2gh, 2gh+1 of token t: gh = r2 / BM,
+    // t = r2 % BM, token t0 + t clamped to the last) and k = i & 7 = tid & 7, so each
+    // quad of lanes reads one whole 128-byte line.  The units are the order of pkq_step
+    // (Q4_K, Q5_K: natural runs), q6_dword and the block-scaled steps.
+    constexpr int IPT = 16 * BM / NTH;
+    static_assert(IPT >= 1 && (16 * BM) % NTH == 0, "token block too small");
     typedef typename MRawOf<T>::type Raw;
     extern __shared__ uint4 lds[];   // two buffers of the block's x for one superblock, 4 * BM * 9 units each
     constexpr int XU = 4 * BM * kUnitsPerTok;
@@ -90,9 +70,17 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
                              : (T == T_FP8 ? A.scales + (rc >> 7) * (A.row_bytes / 64) : nullptr);
     }
     const KqLane L = kq_lane_consts(g);
-    const _Float16 *xsrc[HPT];
+    const int k8 = tid & 7;
+    const uint8_t *xbase = reinterpret_cast<const uint8_t *>(A.x) + t0 * (int64_t)(2 * A.k);   // uniform
+    uint32_t xoff[IPT];   // item v's bytes from xbase, superblock 0 (< 2^27: t < BM, 2k <= 2^21)
+    uint4 *xdst[IPT];     // its unit group, buffer 0
 #pragma unroll
-    for (int v = 0; v < HPT; ++v) xsrc[v] = p_xsrc<T, BM>(A, t0, tid + NTH * v);
+    for (int v = 0; v < IPT; ++v) {
+        const int r2 = (tid + NTH * v) >> 3, gh = r2 / BM, t = r2 % BM;
+        const int tc = t0 + t < A.n ? t : (int)(A.n - 1 - t0);
+        xoff[v] = (uint32_t)tc * (uint32_t)(2 * A.k) + xp_gbase<T>(gh) + xp_koff<T>(k8);
+        xdst[v] = lds + ((2 * gh + xp_ge<T>(k8)) * BM + t) * kUnitsPerTok;
+    }
 
     f4 acc[NT][NG];
 #pragma unroll
@@ -115,28 +103,26 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
 #pragma unroll
         for (int i = 0; i < NT; ++i) R[i] = mload<T>(wr[i], wo[i], sr[i], b, g, sbs, A.tiled);
     };
-    // x of superblock b: loads into registers, then (after a barrier) into LDS.
-    auto fetch_x = [&](XHalf (&X)[HPT], int b) __attribute__((always_inline)) {
+    // x of superblock b: loads into registers, then into LDS.
+    auto fetch_x = [&](uint4 (&X)[2 * IPT], int b) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < HPT; ++v) {
-            const _Float16 *p = xsrc[v] + (int64_t)b * 256;
-#pragma unroll
-            for (int l = 0; l < 4; ++l) {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(p + xhalf_off<T>(l));
-                X[v].v[l] = make_uint4(w.x, w.y, w.z, w.w);
-            }
+        for (int v = 0; v < IPT; ++v) {
+            const uint8_t *src = xbase + xoff[v] + (int64_t)b * 512;
+            const u32x4 p = *reinterpret_cast<const u32x4 *>(src), q = *reinterpret_cast<const u32x4 *>(src + xp_second<T>());
+            X[2 * v] = make_uint4(p.x, p.y, p.z, p.w);
+            X[2 * v + 1] = make_uint4(q.x, q.y, q.z, q.w);
         }
     };
-    auto commit_x = [&](const XHalf (&X)[HPT], int buf) __attribute__((always_inline)) {
+    auto commit_x = [&](const uint4 (&X)[2 * IPT], int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < HPT; ++v) p_xcommit<T>(tid + NTH * v, X[v], lds + buf * XU);
+        for (int v = 0; v < IPT; ++v) xp_commit<T, true>(k8, true, X[2 * v], X[2 * v + 1], xdst[v] + buf * XU);
     };
 
     // Per superblock b: b+1's weights and x go out, b is computed from x buffer b % 2,
     // b+1's x is written to the other buffer, one barrier.  That buffer was last read
     // by the computation of b-1, which every wave finished before the previous barrier.
     Raw ring0[NT], ring1[NT];
-    XHalf X[HPT];
+    uint4 X[2 * IPT];
     load_w(ring0, 0);
     fetch_x(X, 0);
     commit_x(X, 0);
