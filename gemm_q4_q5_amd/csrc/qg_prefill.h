@@ -18,8 +18,8 @@ struct PrefillArgs {
     int32_t pad;
 };
 
-// The unit of the call's size limit: blocks of 64 tokens x 64 weight rows (the FP8 and
-// NVFP4 workgroups; K-quant workgroups take 64 x 128, so fewer of them).
+// The unit of the call's size limit: blocks of 64 tokens x 64 weight rows (the
+// workgroups take 64 x 128, so fewer of them).
 constexpr int kPrefillBlockM = 64, kPrefillBlockN = 64;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
 

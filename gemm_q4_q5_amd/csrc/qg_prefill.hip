@@ -181,20 +181,21 @@ static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
 }
 
 // 64 tokens per workgroup, one 16-row tile per wave and four token groups: 128 weight
-// rows in eight waves for the K-quants, 64 rows in four for FP8 and NVFP4.  Measured
-// at 512 tokens (Q4_K 9728x2560 / Q6_K 2560x9728 / Q5_K 4096x2560, µs): eight waves
-// 61.0 / 88.0 / 31.1 against 62.2 / 89.4 / 33.8 with four (each wave's work is the
-// same; a block's x is staged by twice the threads, so each holds half as much of it
-// in registers); 128 tokens in eight waves 87.4 / 145.7 / 46.8; 32 tokens in four
-// 64.5 / 97.8 / 38.9; earlier, two tiles per wave (64 x 128 in four waves) or 128
-// tokens in four waves spilled registers or left CUs idle.
+// rows in eight waves.  Measured at 512 tokens (Q4_K 9728x2560 / Q6_K 2560x9728 /
+// Q5_K 4096x2560, µs): eight waves 61.0 / 88.0 / 31.1 against 62.2 / 89.4 / 33.8 with
+// four (each wave's work is the same; a block's x is staged by twice the threads, so
+// each holds half as much of it in registers); 128 tokens in eight waves 87.4 / 145.7
+// / 46.8; 32 tokens in four 64.5 / 97.8 / 38.9; earlier, two tiles per wave (64 x 128
+// in four waves) or 128 tokens in four waves spilled registers or left CUs idle.
+// FP8 / NVFP4 (4096 and 16384 rows x 4096, 512 tokens, µs): eight waves 35.2 / 30.4
+// and 118 / 95 against 42.4 / 33.3 and 175 / 116 with four.
 hipError_t launch_prefill(const PrefillArgs &A, hipStream_t st) {
     switch (A.type) {
     case T_Q4_K: return launch_cfg<T_Q4_K, 1, 4, 8>(A, st);
     case T_Q5_K: return launch_cfg<T_Q5_K, 1, 4, 8>(A, st);
     case T_Q6_K: return launch_cfg<T_Q6_K, 1, 4, 8>(A, st);
-    case T_FP8: return launch_cfg<T_FP8, 1, 4, 4>(A, st);
-    default: return launch_cfg<T_NVFP4, 1, 4, 4>(A, st);
+    case T_FP8: return launch_cfg<T_FP8, 1, 4, 8>(A, st);
+    default: return launch_cfg<T_NVFP4, 1, 4, 8>(A, st);
     }
 }
 
