@@ -211,13 +211,17 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
         // 16-wave workgroups (10-wave ones where they give a larger grid).  Without such a grid (large matrices), the most phases
         // per wave and 8-wave workgroups.  Measured at 8 / 16 / 32 tokens (cold rotations, us):
         // the gate/up pair 15.4 -> 13.4 / 15.9 -> 14.4 / 21.0 -> 19.3 (two phases,
-        // 16 waves, 152 workgroups) against the next best choices; the Q6_K down
-        // 2560x9728 keeps 160 workgroups of 8 waves with two phases (26.9 at 32
-        // tokens, 27.9 with 16 waves and one phase), Wo 2560x4096 160 of 8 with one
-        // (11.9; 14.3 with two).
+        // 16 waves, 152 workgroups) against the next best choices; Wo 2560x4096 keeps
+        // 160 workgroups of 8 waves with one phase (11.9; 14.3 with two).
         // Ten-wave workgroups (five tiles of two phases, plain launches) fill more CUs
         // where the tiles do not divide evenly into 8 or 16 per workgroup.
-        static const int kPref[8][2] = {{16, 2}, {10, 2}, {8, 2}, {16, 4}, {8, 4}, {16, 1}, {8, 1}, {4, 1}};
+        // With 16 phases and two token groups, one phase per wave in 16-wave workgroups
+        // comes before two in 8-wave ones (equal grids): 2560x9728 at 17 / 24 / 32 tokens,
+        // Q5_K 17.6 -> 17.0 / 21.0 -> 20.0 / 22.8 -> 21.7 us, Q6_K 16.3 -> 16.0 / 19.4 ->
+        // 18.5 / 21.5 -> 20.3 (at 16 tokens and with 4 phases the other way round).
+        static const int kPrefA[8][2] = {{16, 2}, {10, 2}, {8, 2}, {16, 4}, {8, 4}, {16, 1}, {8, 1}, {4, 1}};
+        static const int kPrefB[8][2] = {{16, 2}, {10, 2}, {16, 1}, {8, 2}, {16, 4}, {8, 4}, {8, 1}, {4, 1}};
+        const int(&kPref)[8][2] = (ng == 2 && ksmax >= 16) ? kPrefB : kPrefA;
         bool dec4 = true;   // every matrix takes the decode path in 4-wave workgroups
         for (int s = 0; s < a.nseg; ++s) dec4 = dec4 && dec_ok(s, 4);
         int best = 0;
