@@ -190,6 +190,12 @@ int run_mma(const qg_weight *const *w, float *const *y, const float *resid, int 
                     break;
                 }
         }
+        // 16 phases from 3 tokens on: each decode-path wave would stage its x in two
+        // rounds, the first waited for before any weight load; two phases per wave in
+        // 8-wave workgroups instead (2560x9728 at 3 / 4 / 6 / 7 tokens, Q6_K 12.0 -> 11.6 /
+        // 12.3 -> 11.9 / 12.7 -> 12.2 / 12.9 -> 12.5 us, Q5_K at 4 / 6 tokens 12.1 -> 12.0 /
+        // 12.7 -> 12.4; at 2 tokens the decode path stays: 9.0 against 11.4).
+        if (ksmax >= 16 && n >= 3 && !sw && one_type && ksmin >= 2 && np < 2) np = 2;
         np = std::max(np, np_min);
         if (np > 1) any_dec = false;
         // The general path takes at least eight waves per workgroup and doubles them
