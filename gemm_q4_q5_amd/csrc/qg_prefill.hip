@@ -31,7 +31,7 @@
 
 namespace qg {
 
-template <int T, int NT, int NG, int WV>
+template <int T, int NT, int NG, int WV, int DEPTH>
 __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A) {
     constexpr int BM = 16 * NG, BN = 16 * WV * NT, NTH = 64 * WV;
     // x staging by 32-byte items (xp_koff, xp_gbase, xp_commit): for a superblock the
@@ -118,37 +118,69 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
         for (int v = 0; v < IPT; ++v) xp_commit<T, true>(k8, true, X[2 * v], X[2 * v + 1], xdst[v] + buf * XU);
     };
 
-    // Per superblock b: b+1's weights and x go out, b is computed from x buffer b % 2,
-    // b+1's x is written to the other buffer, one barrier.  That buffer was last read
-    // by the computation of b-1, which every wave finished before the previous barrier.
-    Raw ring0[NT], ring1[NT];
     uint4 X[2 * IPT];
-    load_w(ring0, 0);
-    fetch_x(X, 0);
-    commit_x(X, 0);
-    __syncthreads();
-    // Two superblocks per trip so that the ring slots and buffers are compile-time.  The
-    // loads are unconditional (the superblock index clamped to the last one; a redundant
-    // load at the end): loads under a branch make the compiler wait for them at the join.
-    // The scheduling barriers keep them ahead of the computation (left alone, the
-    // compiler sinks them to its end, which exposes their whole latency).
-    for (int b = 0; b < nb; b += 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(ring1, min(b + 1, nb - 1));
-        fetch_x(X, min(b + 1, nb - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(ring0, 0);
-        if (b + 1 >= nb) break;   // uniform
-        commit_x(X, 1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(ring0, min(b + 2, nb - 1));
-        fetch_x(X, min(b + 2, nb - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(ring1, 1);
-        if (b + 2 >= nb) break;
+    if constexpr (DEPTH == 2) {
+        // Per superblock b: b+1's weights and x go out, b is computed from x buffer b % 2,
+        // b+1's x is written to the other buffer, one barrier.  That buffer was last read
+        // by the computation of b-1, which every wave finished before the previous barrier.
+        Raw ring0[NT], ring1[NT];
+        load_w(ring0, 0);
+        fetch_x(X, 0);
         commit_x(X, 0);
         __syncthreads();
+        // Two superblocks per trip so that the ring slots and buffers are compile-time.  The
+        // loads are unconditional (the superblock index clamped to the last one; a redundant
+        // load at the end): loads under a branch make the compiler wait for them at the join.
+        // The scheduling barriers keep them ahead of the computation (left alone, the
+        // compiler sinks them to its end, which exposes their whole latency).
+        for (int b = 0; b < nb; b += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(ring1, min(b + 1, nb - 1));
+            fetch_x(X, min(b + 1, nb - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ring0, 0);
+            if (b + 1 >= nb) break;   // uniform
+            commit_x(X, 1);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(ring0, min(b + 2, nb - 1));
+            fetch_x(X, min(b + 2, nb - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ring1, 1);
+            if (b + 2 >= nb) break;
+            commit_x(X, 0);
+            __syncthreads();
+        }
+    } else {
+        // Weights DEPTH superblocks deep: b+DEPTH-1's weights go out while b is computed
+        // (x still one ahead, from the L2), so a superblock's HBM latency is covered by
+        // DEPTH-1 computations.  b+1's x is fetched before the weights: loads complete in
+        // order, and its commit must not wait for the weights just issued.  DEPTH
+        // superblocks per trip (ring slots compile-time), the x buffer b % 2 at run time.
+        Raw ring[DEPTH][NT];
+#pragma unroll
+        for (int s = 0; s + 1 < DEPTH; ++s) load_w(ring[s], min(s, nb - 1));
+        fetch_x(X, 0);
+        commit_x(X, 0);
+        __syncthreads();
+        for (int b = 0; b < nb; b += DEPTH) {
+            bool last = false;
+#pragma unroll
+            for (int s = 0; s < DEPTH; ++s) {
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_x(X, min(b + s + 1, nb - 1));
+                load_w(ring[(s + DEPTH - 1) % DEPTH], min(b + s + DEPTH - 1, nb - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(ring[s], (b + s) & 1);
+                if (b + s + 1 >= nb) {   // uniform
+                    last = true;
+                    break;
+                }
+                commit_x(X, (b + s + 1) & 1);
+                __syncthreads();
+            }
+            if (last) break;
+        }
     }
 
     // D tile (i, q): lane holds tokens 16q + 4g + e, weight row 16i + j of the wave's rows.
@@ -165,18 +197,18 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
     }
 }
 
-template <int T, int NT, int NG, int WV>
+template <int T, int NT, int NG, int WV, int DEPTH>
 static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
     constexpr int BM = 16 * NG, BN = 16 * WV * NT;
     const int64_t blocks = (A.m + BN - 1) / BN * ((A.n + BM - 1) / BM);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)2 * 4 * BM * kUnitsPerTok * 16;   // two x buffers
-    const void *fn = (const void *)prefill_kernel<T, NT, NG, WV>;
+    const void *fn = (const void *)prefill_kernel<T, NT, NG, WV, DEPTH>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_kernel<T, NT, NG, WV>), dim3((unsigned)blocks), dim3(64 * WV), lds, st, A);
+    hipLaunchKernelGGL((prefill_kernel<T, NT, NG, WV, DEPTH>), dim3((unsigned)blocks), dim3(64 * WV), lds, st, A);
     return hipGetLastError();
 }
 
@@ -188,14 +220,18 @@ static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
 // / 46.8; 32 tokens in four 64.5 / 97.8 / 38.9; earlier, two tiles per wave (64 x 128
 // in four waves) or 128 tokens in four waves spilled registers or left CUs idle.
 // FP8 / NVFP4 (4096 and 16384 rows x 4096, 512 tokens, µs): eight waves 35.2 / 30.4
-// and 118 / 95 against 42.4 / 33.3 and 175 / 116 with four.
+// and 118 / 95 against 42.4 / 33.3 and 175 / 116 with four.  Weights three superblocks
+// deep for Q6_K only (its kernel holds one workgroup per CU either way: 143 -> 177
+// VGPRs): 2560x9728 92.0 -> 84.8 µs, 1024x2560 26.8 -> 25.4; four deep 85.5.  For the
+// others a third ring slot gains nothing or costs the second workgroup per CU (Q4_K
+// 120 -> 149 VGPRs, 63.4 -> 75.2 µs; FP8 16384x4096 114.5 -> 127.3).
 hipError_t launch_prefill(const PrefillArgs &A, hipStream_t st) {
     switch (A.type) {
-    case T_Q4_K: return launch_cfg<T_Q4_K, 1, 4, 8>(A, st);
-    case T_Q5_K: return launch_cfg<T_Q5_K, 1, 4, 8>(A, st);
-    case T_Q6_K: return launch_cfg<T_Q6_K, 1, 4, 8>(A, st);
-    case T_FP8: return launch_cfg<T_FP8, 1, 4, 8>(A, st);
-    default: return launch_cfg<T_NVFP4, 1, 4, 8>(A, st);
+    case T_Q4_K: return launch_cfg<T_Q4_K, 1, 4, 8, 2>(A, st);
+    case T_Q5_K: return launch_cfg<T_Q5_K, 1, 4, 8, 2>(A, st);
+    case T_Q6_K: return launch_cfg<T_Q6_K, 1, 4, 8, 3>(A, st);
+    case T_FP8: return launch_cfg<T_FP8, 1, 4, 8, 2>(A, st);
+    default: return launch_cfg<T_NVFP4, 1, 4, 8, 2>(A, st);
     }
 }
 
