@@ -18,7 +18,8 @@ overhead is not part of the measurement.
 Headline: achieved HBM GB/s (algorithmic bytes / time) at N=1, the figure the
 decode-GEMV pages care about.  Beside it: a plain read of the same weight bytes
 (the read-stream probe, same rotation and call order), the same layer at N=32,
-the 512-token prefill GEMM in TFLOP/s, NVFP4 and block-scaled FP8 at 1/16/32
+the 512-token prefill GEMM in TFLOP/s (on the same tiled copies of its weights; the
+row layout beside it), NVFP4 and block-scaled FP8 at 1/16/32
 rows on 16384x8192 and the 151936x2560 head, and the CPU oracle on a bounded
 sample.
 Prints one JSON line.
@@ -337,9 +338,10 @@ PREFILL_N = 512
 PREFILL_COPIES = 4
 
 
-def _prefill_calls():
+def _prefill_calls(layout="tiles"):
     """calls(only=None): the prefill calls on the three shapes, each over its rotated copies
-    (only = an index into PREFILL for one shape)."""
+    (only = an index into PREFILL for one shape).  layout "tiles": the weights repacked once
+    into 16-row tiles, the copy the decode calls read; "rows": as stored."""
     import torch
     import gemm_q4_q5_amd as qg
     import synth
@@ -347,7 +349,10 @@ def _prefill_calls():
     for i, (name, wt, m, k) in enumerate(PREFILL):
         data, scales = synth.weights(wt, m, k, synth.rng_for(3, i))
         base = qg.QWeight.from_host(wt, data, m, k, scales, device="cuda")
-        ws.append([base] + [qg.QWeight(wt, base.data.clone(), m, k, None) for _ in range(PREFILL_COPIES - 1)])
+        if layout == "tiles":
+            base = qg.pack_tiles(base)
+        ws.append([base] + [qg.QWeight(wt, base.data.clone(), m, k, None, base.layout)
+                            for _ in range(PREFILL_COPIES - 1)])
     rng = synth.rng_for(3, 99)
     xs = {k: torch.from_numpy(synth.activations(PREFILL_N, k, rng)).to("cuda") for k in (2560, 9728)}
     ys = [torch.empty((PREFILL_N, m), dtype=torch.float32, device="cuda") for _, _, m, _ in PREFILL]
@@ -381,11 +386,11 @@ def replay_prefill(name, steps, warmup):
                       "TFLOP/s": round(2.0 * PREFILL_N * m * k / (us * 1e-6) / 1e12, 1)}))
 
 
-def time_prefill(reps=10):
+def time_prefill(reps=10, layout="tiles"):
     """Prefill chunk of 512 tokens through the MFMA GEMM on the three config
     shapes (4 rotated copies of each weight), from a HIP graph."""
     import torch
-    calls = _prefill_calls()
+    calls = _prefill_calls(layout)
     calls()
     torch.cuda.synchronize()
     out = {}
@@ -679,6 +684,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill:
         res["prefill_n512"] = time_prefill()
+        res["prefill_n512_rows_layout"] = time_prefill(layout="rows")
     if not args.no_nvfp4:
         res["nvfp4_large"] = time_scaled(qg.NVFP4)
     if not args.no_fp8:

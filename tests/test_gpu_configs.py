@@ -132,6 +132,10 @@ def test_workload3_prefill_512(j, wt, m, k):
     rows = np.unique(np.concatenate([rows, [m - 1]]))
     y_ref, a = oracle.gemm(wt, data, scales, m, k, x, rows=rows)
     assert_within(y.cpu().numpy()[:, rows], y_ref, a, what=f"prefill type {wt}")
+    # The timed copy: the same weights repacked into 16-row tiles give the same bits.
+    yt = qg.qgemm_prefill(qg.pack_tiles(w), x_dev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), yt.view(torch.int32)), "tiled prefill differs from the row layout"
 
 
 @pytest.fixture(scope="module", params=[(16384, 8192), (151936, 2560)], ids=["16384x8192", "head151936x2560"])
