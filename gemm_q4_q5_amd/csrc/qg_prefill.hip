@@ -31,29 +31,42 @@
 
 namespace qg {
 
-template <int T, int NT, int NG, int WV, int DEPTH>
-__global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A) {
-    constexpr int BM = 16 * NG, BN = 16 * WV * NT, NTH = 64 * WV;
+template <int T, int NT, int NG, int WV, int DEPTH, int KH>
+__global__ __launch_bounds__(64 * WV, (WV <= 8 ? 8 / WV : 1)) void prefill_kernel(PrefillArgs A) {
+    // KH K parts: the WV waves are KH groups of TW row-group waves; part h computes
+    // superblocks [h*nh, h*nh + nh) of the same rows, stages their x in LDS buffers of its
+    // own, and the parts' sums are added in part order at the end (through LDS).
+    static_assert(WV % KH == 0 && (KH == 1 || KH == 2), "K parts");
+    constexpr int TW = WV / KH;
+    constexpr int BM = 16 * NG, BN = 16 * TW * NT, NTH = 64 * TW;   // NTH: threads per part
     // x staging by 32-byte items (xp_koff, xp_gbase, xp_commit): for a superblock the
-    // block's x is 16*BM items; thread tid takes items tid + NTH*v, v < IPT, item i
-    // having record pair r2 = i >> 3 (lane groups 2gh, 2gh+1 of token t: gh = r2 / BM,
-    // t = r2 % BM, token t0 + t clamped to the last) and k = i & 7 = tid & 7, so each
+    // block's x is 16*BM items; thread ptid of a part takes items ptid + NTH*v, v < IPT,
+    // item i having record pair r2 = i >> 3 (lane groups 2gh, 2gh+1 of token t: gh = r2 / BM,
+    // t = r2 % BM, token t0 + t clamped to the last) and k = i & 7 = ptid & 7, so each
     // quad of lanes reads one whole 128-byte line.  The units are the order of pkq_step
     // (Q4_K, Q5_K: natural runs), q6_dword and the block-scaled steps.
-    constexpr int IPT = 16 * BM / NTH;
-    static_assert(IPT >= 1 && (16 * BM) % NTH == 0, "token block too small");
+    // Where NTH does not divide the 16*BM items, a thread's items past the end are the
+    // block's last record pair again (same k): a duplicate load and an identical LDS
+    // write, no branch.
+    constexpr int IPT = (16 * BM + NTH - 1) / NTH;
+    static_assert(16 * BM >= NTH, "token block too small");
     typedef typename MRawOf<T>::type Raw;
-    extern __shared__ uint4 lds[];   // two buffers of the block's x for one superblock, 4 * BM * 9 units each
+    extern __shared__ uint4 lds[];   // per K part two buffers of the block's x for one superblock, 4 * BM * 9 units each
     constexpr int XU = 4 * BM * kUnitsPerTok;
 
     const int tid = (int)threadIdx.x, lane = tid & 63;
-    const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);   // row group
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wv / TW, wq = wv % TW;   // K part, row group (uniform)
+    const int ptid = tid - 64 * TW * kh;    // thread index within the part
     const int j = lane & 15, g = lane >> 4;
     // One-dimensional grid, row blocks fastest.
     const int64_t rblocks = (A.m + BN - 1) / BN;
     const int64_t t0 = (int64_t)blockIdx.x / rblocks * BM;
     const int64_t r0 = (int64_t)blockIdx.x % rblocks * BN + wq * (16 * NT);
     const int nb = A.k / 256;
+    const int nh = (nb + KH - 1) / KH, kb0 = kh * nh;   // superblocks per part (uniform); the part's first
+    const int cnt = min(nh, nb - kb0);                   // the part's own count (the last part may have fewer)
+    auto sbi = [&](int i) __attribute__((always_inline)) { return min(kb0 + i, nb - 1); };
 
     constexpr int S = T == T_Q4_K ? 144 : (T == T_Q5_K ? 176 : (T == T_Q6_K ? 210 : 0));
     const int sbs = A.tiled ? 16 * S : S;
@@ -70,16 +83,17 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
                              : (T == T_FP8 ? A.scales + (rc >> 7) * (A.row_bytes / 64) : nullptr);
     }
     const KqLane L = kq_lane_consts(g);
-    const int k8 = tid & 7;
+    const int k8 = ptid & 7;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(A.x) + t0 * (int64_t)(2 * A.k);   // uniform
     uint32_t xoff[IPT];   // item v's bytes from xbase, superblock 0 (< 2^27: t < BM, 2k <= 2^21)
     uint4 *xdst[IPT];     // its unit group, buffer 0
 #pragma unroll
     for (int v = 0; v < IPT; ++v) {
-        const int r2 = (tid + NTH * v) >> 3, gh = r2 / BM, t = r2 % BM;
+        const int it = min(ptid + NTH * v, 16 * BM - 8 + k8);   // it & 7 == k8 (NTH % 8 == 0)
+        const int r2 = it >> 3, gh = r2 / BM, t = r2 % BM;
         const int tc = t0 + t < A.n ? t : (int)(A.n - 1 - t0);
         xoff[v] = (uint32_t)tc * (uint32_t)(2 * A.k) + xp_gbase<T>(gh) + xp_koff<T>(k8);
-        xdst[v] = lds + ((2 * gh + xp_ge<T>(k8)) * BM + t) * kUnitsPerTok;
+        xdst[v] = lds + kh * XU + ((2 * gh + xp_ge<T>(k8)) * BM + t) * kUnitsPerTok;
     }
 
     f4 acc[NT][NG];
@@ -88,12 +102,14 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
 #pragma unroll
         for (int q = 0; q < NG; ++q) acc[i][q] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    // One superblock: the MFMAs of ring slot R over the x staged in buffer `buf`.
-    const uint4 *xl = lds + (g * BM + j) * kUnitsPerTok;   // the lane's token, step 0
-    auto compute = [&](Raw (&R)[NT], int buf) __attribute__((always_inline)) {
+    // One superblock (the part's i-th): the MFMAs of ring slot R over the x staged in
+    // buffer `buf`; a part with fewer superblocks skips its last step (uniform).
+    const uint4 *xl = lds + kh * XU + (g * BM + j) * kUnitsPerTok;   // the lane's token, step 0
+    auto compute = [&](Raw (&R)[NT], int buf, int i) __attribute__((always_inline)) {
+        if (KH > 1 && i >= cnt) return;
         const uint4 *xa[NG];
 #pragma unroll
-        for (int q = 0; q < NG; ++q) xa[q] = xl + buf * XU + 16 * q * kUnitsPerTok;
+        for (int q = 0; q < NG; ++q) xa[q] = xl + buf * KH * XU + 16 * q * kUnitsPerTok;
         msb<T, NT, NG, true>(R, g, L, xa, acc);
         // The compiler's interleaving of the MFMAs with the operand construction and
         // the x reads (mode 1): 3-4 % faster at 512 tokens than its default order.
@@ -115,7 +131,7 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
     };
     auto commit_x = [&](const uint4 (&X)[2 * IPT], int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < IPT; ++v) xp_commit<T, true>(k8, true, X[2 * v], X[2 * v + 1], xdst[v] + buf * XU);
+        for (int v = 0; v < IPT; ++v) xp_commit<T, true>(k8, true, X[2 * v], X[2 * v + 1], xdst[v] + buf * KH * XU);
     };
 
     uint4 X[2 * IPT];
@@ -124,8 +140,8 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
         // b+1's x is written to the other buffer, one barrier.  That buffer was last read
         // by the computation of b-1, which every wave finished before the previous barrier.
         Raw ring0[NT], ring1[NT];
-        load_w(ring0, 0);
-        fetch_x(X, 0);
+        load_w(ring0, sbi(0));
+        fetch_x(X, sbi(0));
         commit_x(X, 0);
         __syncthreads();
         // Two superblocks per trip so that the ring slots and buffers are compile-time.  The
@@ -133,21 +149,21 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
         // load at the end): loads under a branch make the compiler wait for them at the join.
         // The scheduling barriers keep them ahead of the computation (left alone, the
         // compiler sinks them to its end, which exposes their whole latency).
-        for (int b = 0; b < nb; b += 2) {
+        for (int b = 0; b < nh; b += 2) {
             __builtin_amdgcn_sched_barrier(0);
-            load_w(ring1, min(b + 1, nb - 1));
-            fetch_x(X, min(b + 1, nb - 1));
+            load_w(ring1, sbi(b + 1));
+            fetch_x(X, sbi(b + 1));
             __builtin_amdgcn_sched_barrier(0);
-            compute(ring0, 0);
-            if (b + 1 >= nb) break;   // uniform
+            compute(ring0, 0, b);
+            if (b + 1 >= nh) break;   // uniform
             commit_x(X, 1);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            load_w(ring0, min(b + 2, nb - 1));
-            fetch_x(X, min(b + 2, nb - 1));
+            load_w(ring0, sbi(b + 2));
+            fetch_x(X, sbi(b + 2));
             __builtin_amdgcn_sched_barrier(0);
-            compute(ring1, 1);
-            if (b + 2 >= nb) break;
+            compute(ring1, 1, b + 1);
+            if (b + 2 >= nh) break;
             commit_x(X, 0);
             __syncthreads();
         }
@@ -159,20 +175,20 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
         // superblocks per trip (ring slots compile-time), the x buffer b % 2 at run time.
         Raw ring[DEPTH][NT];
 #pragma unroll
-        for (int s = 0; s + 1 < DEPTH; ++s) load_w(ring[s], min(s, nb - 1));
-        fetch_x(X, 0);
+        for (int s = 0; s + 1 < DEPTH; ++s) load_w(ring[s], sbi(s));
+        fetch_x(X, sbi(0));
         commit_x(X, 0);
         __syncthreads();
-        for (int b = 0; b < nb; b += DEPTH) {
+        for (int b = 0; b < nh; b += DEPTH) {
             bool last = false;
 #pragma unroll
             for (int s = 0; s < DEPTH; ++s) {
                 __builtin_amdgcn_sched_barrier(0);
-                fetch_x(X, min(b + s + 1, nb - 1));
-                load_w(ring[(s + DEPTH - 1) % DEPTH], min(b + s + DEPTH - 1, nb - 1));
+                fetch_x(X, sbi(b + s + 1));
+                load_w(ring[(s + DEPTH - 1) % DEPTH], sbi(b + s + DEPTH - 1));
                 __builtin_amdgcn_sched_barrier(0);
-                compute(ring[s], (b + s) & 1);
-                if (b + s + 1 >= nb) {   // uniform
+                compute(ring[s], (b + s) & 1, b + s);
+                if (b + s + 1 >= nh) {   // uniform
                     last = true;
                     break;
                 }
@@ -181,6 +197,29 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
             }
             if (last) break;
         }
+    }
+
+    if constexpr (KH == 2) {
+        // Part 1's sums through LDS (every wave is past its last x read), added to part
+        // 0's in that order; part 0 stores.
+        __syncthreads();
+        float *red = reinterpret_cast<float *>(lds) + wq * (NT * NG * 4 * 64) + lane;
+        if (kh == 1) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int q = 0; q < NG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) red[((i * NG + q) * 4 + e) * 64] = acc[i][q][e];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][q][e] += red[((i * NG + q) * 4 + e) * 64];
     }
 
     // D tile (i, q): lane holds tokens 16q + 4g + e, weight row 16i + j of the wave's rows.
@@ -197,18 +236,19 @@ __global__ __launch_bounds__(64 * WV, 8 / WV) void prefill_kernel(PrefillArgs A)
     }
 }
 
-template <int T, int NT, int NG, int WV, int DEPTH>
+template <int T, int NT, int NG, int WV, int DEPTH, int KH = 1>
 static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
-    constexpr int BM = 16 * NG, BN = 16 * WV * NT;
+    constexpr int BM = 16 * NG, BN = 16 * (WV / KH) * NT;
     const int64_t blocks = (A.m + BN - 1) / BN * ((A.n + BM - 1) / BM);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)2 * 4 * BM * kUnitsPerTok * 16;   // two x buffers
-    const void *fn = (const void *)prefill_kernel<T, NT, NG, WV, DEPTH>;
+    const size_t lds = (size_t)2 * KH * 4 * BM * kUnitsPerTok * 16;   // two x buffers per K part
+    static_assert((size_t)2 * KH * 4 * BM * kUnitsPerTok * 16 >= (size_t)(WV / KH) * NT * NG * 4 * 64 * 4, "reduction");
+    const void *fn = (const void *)prefill_kernel<T, NT, NG, WV, DEPTH, KH>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_kernel<T, NT, NG, WV, DEPTH>), dim3((unsigned)blocks), dim3(64 * WV), lds, st, A);
+    hipLaunchKernelGGL((prefill_kernel<T, NT, NG, WV, DEPTH, KH>), dim3((unsigned)blocks), dim3(64 * WV), lds, st, A);
     return hipGetLastError();
 }
 
@@ -225,11 +265,19 @@ static hipError_t launch_cfg(const PrefillArgs &A, hipStream_t st) {
 // VGPRs): 2560x9728 92.0 -> 84.8 µs, 1024x2560 26.8 -> 25.4; four deep 85.5.  For the
 // others a third ring slot gains nothing or costs the second workgroup per CU (Q4_K
 // 120 -> 149 VGPRs, 63.4 -> 75.2 µs; FP8 16384x4096 114.5 -> 127.3).
+constexpr int64_t kPrefillCUs = 256;   // MI355X compute units
 hipError_t launch_prefill(const PrefillArgs &A, hipStream_t st) {
     switch (A.type) {
     case T_Q4_K: return launch_cfg<T_Q4_K, 1, 4, 8, 2>(A, st);
     case T_Q5_K: return launch_cfg<T_Q5_K, 1, 4, 8, 2>(A, st);
-    case T_Q6_K: return launch_cfg<T_Q6_K, 1, 4, 8, 3>(A, st);
+    case T_Q6_K: {
+        // Too few 128-row blocks to fill the chip (the 2560-row down projection: 160
+        // workgroups): 80-row blocks in ten waves, five row tiles times two K halves.
+        const int64_t tb = (A.n + 63) / 64;
+        if (A.k >= 512 && (A.m + 127) / 128 * tb < kPrefillCUs && (A.m + 79) / 80 * tb <= kPrefillCUs)
+            return launch_cfg<T_Q6_K, 1, 4, 10, 2, 2>(A, st);
+        return launch_cfg<T_Q6_K, 1, 4, 8, 3>(A, st);
+    }
     case T_FP8: return launch_cfg<T_FP8, 1, 4, 8, 2>(A, st);
     default: return launch_cfg<T_NVFP4, 1, 4, 8, 2>(A, st);
     }

@@ -23,10 +23,13 @@ TYPES = [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4, qg.FP8]
 
 
 @pytest.mark.parametrize("wt", TYPES)
-# 64-token x 64-row blocks: one superblock (k = 256) up to 4 (k = 1024); ragged in
+# 64-token x 128-row blocks: one superblock (k = 256) up to 9 (k = 2304); ragged in
 # tokens and rows (a last block with 1..63 of each); one block, and grids of thousands.
+# Q6_K grids of fewer than 256 such blocks run as 80-row blocks of two K halves (an odd
+# superblock count leaves the second half one short): (300, 1024), (130, 768),
+# (1000, 512, 256) and (2500, 2304, 500).
 @pytest.mark.parametrize("m,k,n", [(300, 1024, 130), (64, 256, 1), (130, 768, 17), (1000, 512, 256),
-                                   (2000, 256, 2050), (1000, 512, 2000), (1000, 256, 2100)])
+                                   (2000, 256, 2050), (1000, 512, 2000), (1000, 256, 2100), (2500, 2304, 500)])
 def test_prefill_vs_oracle(wt, m, k, n):
     import torch
     print(f"prefill type={wt} m={m} k={k} n={n}", flush=True)
