@@ -18,9 +18,11 @@
 // Q4_K / Q5_K quant dwords are byte-paired first, so that x is staged without
 // permutes.  No weight is rounded except a Q6_K one with |sc| > 64 (once, to fp16).
 //
-// Per superblock b: b+1's weights and x are loaded into registers while b is
-// computed; a barrier; b+1's x is written to the (single) LDS buffer; a barrier.
-// Several workgroups share a CU, so one's barriers overlap another's MFMAs.  Loads
+// Per superblock b: b+1's weights (Q6_K: b+2's) and x are loaded into registers while
+// b is computed from one of two LDS x buffers; b+1's x is written to the other; one
+// barrier.  Where two workgroups share a CU, one's barrier overlaps the other's MFMAs.
+// Where 128-row blocks would leave CUs idle, Q6_K workgroups take 80 rows in two K
+// halves whose sums are added in order at the end.  Loads
 // past the last token or weight row are clamped to the last one (every address
 // stays in bounds); those rows are never stored.  No row-invariance contract
 // (TandemLLM Kernels page, "Prefill kernels"): the result is deterministic, but not
