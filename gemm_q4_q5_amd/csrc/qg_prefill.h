@@ -19,7 +19,7 @@ struct PrefillArgs {
 };
 
 // The unit of the call's size limit: blocks of 64 tokens x 64 weight rows (the
-// workgroups take 64 x 128, so fewer of them).
+// workgroups take 64 x 128, or 64 x 80 for Q6_K in two K halves, so fewer of them).
 constexpr int kPrefillBlockM = 64, kPrefillBlockN = 64;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
 
