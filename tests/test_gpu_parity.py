@@ -241,6 +241,28 @@ def test_phases_per_wave_keep_rows_bit_identical(wt):
     assert_within(y.cpu().numpy()[:, rows], y_ref, a, what=f"phases type {wt}")
 
 
+# The layer's Q6_K down projection (160 row tiles, 16 phases): one token on the decode
+# path, 3..7 tokens two phases per wave in 8-wave workgroups, from 8 tokens the general
+# path's grid search; every row keeps the bits of its one-token call.
+def test_down_shape_bits_across_launch_shapes():
+    import torch
+    m, k = 2560, 9728
+    w, data, scales = weight(qg.Q6_K, m, k, 305)
+    x = synth.duplicate_rows(synth.activations(32, k, synth.rng_for(306)))
+    xd = x_dev(x)
+    singles = [bits(qg.qgemv(w, xd[t])) for t in range(32)]
+    for n in (2, 3, 4, 5, 6, 7, 8, 9, 17, 32):
+        print(f"down {m}x{k} n={n}", flush=True)
+        yb = bits(qg.qgemm_rows(w, xd[:n]))
+        for t in range(n):
+            assert np.array_equal(yb[t], singles[t]), f"n={n} row {t} differs from n=1"
+    y = qg.qgemm_rows(w, xd[:7])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, m - 1], synth.rng_for(307).choice(m, size=64, replace=False)]))
+    y_ref, a = oracle.gemm(qg.Q6_K, data, scales, m, k, x[:7], rows=rows)
+    assert_within(y.cpu().numpy()[:, rows], y_ref, a, what="down 7 tokens")
+
+
 # The gate/up pair at the layer's shape: the launch shape changes with n (decode path
 # below 8 tokens, two phases per wave in 16-wave workgroups from 8 on); each output
 # must equal the plain call on its matrix, and every row its one-token call, bit for bit.
