@@ -30,6 +30,7 @@ def test_graph_replays_equal_eager_calls():
         out["add"] = qg.qgemv_add(wq, x, resid, out.get("add"))
         out["sw"] = qg.qgemv_pair_swiglu(wk, wk, x, out.get("sw"))
         out["pf"] = qg.qgemm_prefill(wq, xp, out.get("pf"))
+        out["pf6"] = qg.qgemm_prefill(wv, xp, out.get("pf6"))   # Q6_K: the two K halves
         return out
 
     side = torch.cuda.Stream()
